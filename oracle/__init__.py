@@ -1,0 +1,55 @@
+"""CPU float64 oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library; both are fed the same seeded inputs by the test harness.
+
+Sources (the three pages on FlashAttention):
+  * "FlashAttention: The Matrix You Never Have to Write Down"
+    (maitreyasuin.github.io) -- sections "What attention computes",
+    "What stops us", "The identity", "From softmax to attention", "Build it",
+    "Check it", "Causal masking".
+  * "Why FlashAttention Can Avoid a Square Attention Array Without Making
+    Attention Linear" (leviathansystems.co) -- sections "Tiles need a shared
+    softmax normalization", "A two-block example", "Backward can recreate
+    tiles".
+
+Functions and what pins each one (tests/test_oracle.py):
+  attention_forward   plain materialised definition.  Pinned by the two-block
+                      example (20/3), the late-max example, uniform-score
+                      closed form, brute-force per-row loops, torch SDPA.
+  attention_backward  chain rule on the definition (the pages give no
+                      gradient equations; this is the textbook derivation).
+                      Pinned by central finite differences, by torch
+                      autograd of a float64 softmax, and by the row-sum
+                      invariants of dK and dV.
+  tiled_forward       the pages' blocked recurrence, used to show that the
+                      online rescale reaches the one-shot result.  Pinned by
+                      the two-block example, the late max, the causal tile
+                      counts (36/64, 528/1024) and equality with
+                      attention_forward on ragged block sizes.
+  streaming_logsumexp the one-pass (max, sum) reduction with its two guards.
+                      Pinned by the four-number example and the seeded
+                      1000-value example printed on the first page.
+"""
+
+from .attention import (
+    attention_forward,
+    attention_backward,
+    attention_forward_bhnd,
+    attention_backward_bhnd,
+    tiled_forward,
+    streaming_logsumexp,
+    online_normalizer_trace,
+)
+
+__all__ = [
+    "attention_forward",
+    "attention_backward",
+    "attention_forward_bhnd",
+    "attention_backward_bhnd",
+    "tiled_forward",
+    "streaming_logsumexp",
+    "online_normalizer_trace",
+]
