@@ -1,0 +1,152 @@
+"""Exact IO-aware attention for MI355X (gfx950): Python binding of libfa.so.
+
+Thin ctypes marshalling over the C ABI declared in include/fa.h: it checks
+the inputs the way the first page's reference implementation does (rank,
+floating dtype, matching dtypes, widths, lengths, devices), allocates the
+outputs with torch on the inputs' device and passes raw device pointers and
+the current HIP stream.  Every arithmetic step runs in the library's
+kernels; there is no fallback.  If libfa.so has not been built this raises.
+
+    o, lse = forward(q, k, v, causal=False)          # q,k,v: [B,H,N,d] bf16 or f32
+    dq, dk, dv = backward(q, k, v, o, lse, do, causal=False)
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["forward", "backward", "library", "FAError", "LIB_PATH", "status_string"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-zero fa_status returned by the library."""
+
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def library():
+    """The loaded libfa.so (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_16_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_fwd.restype = i
+        lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_fwd_f32.restype = i
+        lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd.restype = i
+        lib.fa_status_string.argtypes = [i]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status):
+    return library().fa_status_string(int(status)).decode()
+
+
+def _check(q, k, v):
+    """Input contract: the page's single-head checks, extended to [B, H, N, d]."""
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("Q, K, V must be rank 4 [B, H, N, d]")
+    if not all(t.is_floating_point() for t in (q, k, v)):
+        raise TypeError("Q, K, V must be floating point")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError(f"dtypes differ: {q.dtype}, {k.dtype}, {v.dtype}")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported dtype {q.dtype} (bfloat16 or float32)")
+    if k.shape[-1] != q.shape[-1]:
+        raise ValueError(f"Q and K widths differ: {q.shape[-1]} vs {k.shape[-1]}")
+    if v.shape[-2] != k.shape[-2]:
+        raise ValueError(f"K and V lengths differ: {k.shape[-2]} vs {v.shape[-2]}")
+    if q.shape[-1] == 0:
+        raise ValueError("query/key width must be positive")
+    if not (q.device == k.device == v.device):
+        raise ValueError("Q, K, V must be on the same device")
+    if q.shape != k.shape or k.shape != v.shape:
+        raise ValueError(f"Q, K, V must share one [B, H, N, d] shape, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if q.device.type != "cuda":
+        raise ValueError("Q, K, V must be GPU tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("Q, K, V must be contiguous")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Exact attention: returns (O float32 [B,H,N,d], L float32 [B,H,N]).
+
+    L is the natural-log logsumexp of the scaled, masked scores of each row.
+    bf16 inputs run the matrix-core kernel (fa_fwd); float32 inputs run the
+    float32 kernel (fa_fwd_f32).  ``out``/``lse`` may be preallocated.
+    """
+    _check(q, k, v)
+    B, H, N, d = q.shape
+    o = out if out is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    l = lse if lse is not None else torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    lib = library()
+    fn = lib.fa_fwd if q.dtype == torch.bfloat16 else lib.fa_fwd_f32
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d, _scale(scale, d), int(bool(causal)),
+            _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_fwd" if q.dtype == torch.bfloat16 else "fa_fwd_f32", st)
+    return o, l
+
+
+def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
+    """Gradients (dQ, dK, dV), float32 [B,H,N,d], of sum(dO * O).
+
+    ``o`` and ``lse`` must be the forward's outputs for the same inputs; the
+    probability tiles are recomputed from them.  bf16 inputs only.
+    """
+    _check(q, k, v)
+    if q.dtype != torch.bfloat16 or do.dtype != torch.bfloat16:
+        raise TypeError("backward takes bfloat16 Q, K, V and dO")
+    if do.shape != q.shape or o.shape != q.shape or lse.shape != q.shape[:3]:
+        raise ValueError("dO and O must match Q's shape and L must be [B, H, N]")
+    if o.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise TypeError("O and L must be float32 (as returned by forward)")
+    if not (do.is_contiguous() and o.is_contiguous() and lse.is_contiguous()):
+        raise ValueError("dO, O and L must be contiguous")
+    if not (do.device == o.device == lse.device == q.device):
+        raise ValueError("all tensors must be on the same device")
+    B, H, N, d = q.shape
+    lib = library()
+    ws_bytes = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace too small: need {ws_bytes} bytes")
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                    _ptr(workspace), B, H, N, d, _scale(scale, d), int(bool(causal)), _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_bwd", st)
+    return dq, dk, dv

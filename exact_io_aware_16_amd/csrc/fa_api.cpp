@@ -1,0 +1,92 @@
+// C ABI of libfa.so: host-side argument checks, then the kernel launches.
+// Every check runs before anything touches the HIP runtime, so invalid
+// arguments return an fa_status code without a device present.
+#include "../../include/fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.h"
+
+namespace {
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// Validates shape arguments; sets *empty when there is nothing to compute.
+int check_shape(int B, int H, int N, int d, int causal, bool* empty) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  *empty = (B == 0 || H == 0 || N == 0);
+  // element offsets are computed in 64 bits; B*H must fit an int and the
+  // total element count must stay well inside 2^62
+  const long long bh = (long long)B * H;
+  if (bh > INT32_MAX) return FA_ERR_SHAPE;
+  if ((double)bh * N * d > 4.0e18) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, scale, causal, stream));
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  return hip_status(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, scale, causal, stream));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  bool empty = false;
+  if (check_shape(B, H, N, d, 0, &empty) != FA_OK || empty) return 0;
+  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+           float* dq, float* dk, float* dv, void* workspace, int B, int H, int N, int d, float scale, int causal,
+           hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!workspace) return FA_ERR_WORKSPACE;
+  return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
+                                        N, d, scale, causal, stream));
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (negative B/H/N, causal not 0/1, or size overflow)";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_WORKSPACE: return "backward workspace is NULL";
+    case FA_ERR_HIP: return "HIP runtime rejected a kernel launch";
+    default: return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

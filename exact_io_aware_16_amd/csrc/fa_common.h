@@ -1,0 +1,74 @@
+// Device-side building blocks shared by the attention kernels (gfx950).
+//
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16, one
+// 64-lane wave, lane l, half g = l / 32, column c = l % 32):
+//   A operand (32 x 16, row-major M x K): lane holds A[c][8g .. 8g+7]
+//   B operand (16 x 32, K x N):           lane holds B[8g .. 8g+7][c]
+//   C result  (32 x 32):                  register i holds C[8(i/4) + 4g + i%4][c]
+// So every operand register group is 8 consecutive elements along the
+// contraction axis, and a result column belongs to one lane.  The row order
+// of the result can be chosen freely by choosing which source row each lane
+// loads as A row c; the kernels use the bit permutation perm32 (swap bits 2
+// and 3 of the row index) so that register i of half g lands on row
+// 16(i/8) + 8g + i%8: runs of 8 consecutive rows per register octet, which
+// is exactly the operand layout of the next product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_raw;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// swap bits 2 and 3 of a row index in 0..31 (an involution)
+__device__ __forceinline__ constexpr int perm32(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// result register i of half g of a perm32-loaded product -> row in 0..31
+__device__ __forceinline__ constexpr int perm_row(int i, int g) {
+  return 16 * (i / 8) + 8 * g + (i % 8);
+}
+
+// plain (unpermuted) result row of register i in half g
+__device__ __forceinline__ constexpr int acc_row(int i, int g) {
+  return 8 * (i / 4) + 4 * g + (i % 4);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Eight float32 values rounded to bf16 (round to nearest even) and packed.
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)p[e];
+  return r;
+}
+
+// Workgroup order: the hardware hands consecutive workgroup ids to the eight
+// XCDs in turn, and each XCD has its own L2.  Mapping id -> (id % 8) * per +
+// id / 8 gives XCD x the contiguous logical range [x*per, (x+1)*per), so the
+// query blocks of one head -- which stream the same K and V -- share an L2.
+// grid must be a multiple of 8; ids mapping past `total` do nothing.
+__device__ __forceinline__ int xcd_logical_block(int bid, int grid) {
+  const int per = grid >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+}  // namespace fa

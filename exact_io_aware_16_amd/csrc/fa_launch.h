@@ -1,0 +1,20 @@
+// Internal host-side launchers; called by the C ABI in fa_api.cpp after all
+// arguments have been validated.  BH = B * H.  Each returns the HIP status of
+// its launches (hipSuccess when everything was enqueued).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+namespace fa {
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int N,
+                           int d, float scale, int causal, hipStream_t stream);
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N,
+                          int d, float scale, int causal, hipStream_t stream);
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                           const void* dout, float* dq, float* dk, float* dv, float* dvec, int BH, int N,
+                           int d, float scale, int causal, hipStream_t stream);
+
+}  // namespace fa

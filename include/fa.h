@@ -1,0 +1,109 @@
+/*
+ * fa.h -- C ABI of the exact IO-aware attention library (libfa.so, gfx950).
+ *
+ * The library computes exact scaled-dot-product attention,
+ *     O = softmax(scale * Q K^T) V,      L = logsumexp(scale * Q K^T) (natural log),
+ * block by block with an online softmax, so no N x N score or probability
+ * matrix is ever written to device memory, and its gradient by recomputing
+ * the probability tiles from Q, K and the saved L.
+ *
+ * Sources: "FlashAttention: The Matrix You Never Have to Write Down"
+ * (maitreyasuin.github.io), sections "What attention computes", "The
+ * identity", "From softmax to attention", "Build it", "Causal masking" and
+ * "The forward pass is only half of it"; "Why FlashAttention Can Avoid a
+ * Square Attention Array Without Making Attention Linear"
+ * (leviathansystems.co), sections "Tiles need a shared softmax
+ * normalization" and "Backward can recreate tiles instead of retaining the
+ * square".
+ *
+ * Conventions shared by every entry point
+ *  - Layout: every [B,H,N,d] tensor is dense row-major with d innermost
+ *    (element (b,h,n,c) at ((b*H + h)*N + n)*d + c); L and the backward
+ *    workspace rows are [B,H,N].  Q, K, V (and dO) are bf16 except for
+ *    fa_fwd_f32; O, L, dQ, dK, dV are float32.
+ *  - Causal masking is upper-left: query n sees keys 0..n (the
+ *    is_causal=True convention of torch SDPA), "Build it" note on
+ *    alignment.  causal is 0 or 1.
+ *  - Memory: the caller allocates every buffer in device memory (hipMalloc or
+ *    torch); the library never allocates, frees or synchronises.  Inputs are
+ *    read only; outputs must not overlap inputs or each other.
+ *  - Execution: work is enqueued on `stream` (NULL = the null stream) and
+ *    the call returns at once; results are ready when the caller
+ *    synchronises that stream.  Kernel faults surface at that point.
+ *  - Errors: all arguments are checked on the host before anything is
+ *    enqueued; on error nothing is launched and an fa_status code is
+ *    returned.  B, H or N equal to 0 is a valid empty problem: FA_OK,
+ *    nothing launched.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = 2,     /* B, H or N negative, causal not 0/1, or size overflow */
+  FA_ERR_HEADDIM = 3,   /* d is not a supported head width (64 or 128)         */
+  FA_ERR_SCALE = 4,     /* scale is not finite and > 0                         */
+  FA_ERR_WORKSPACE = 5, /* backward workspace missing                          */
+  FA_ERR_HIP = 6        /* a kernel launch was rejected by the HIP runtime     */
+} fa_status;
+
+/*
+ * Forward pass, bf16 inputs ("From softmax to attention" and "Build it").
+ *   q, k, v : device, bf16 [B,H,N,d]
+ *   o       : device, float32 [B,H,N,d]  -- normalised output
+ *   lse     : device, float32 [B,H,N]    -- per-row logsumexp of the scaled,
+ *             masked scores, natural log; the statistic the backward needs
+ *   d       : 64 or 128;  scale > 0 and finite (usually 1/sqrt(d))
+ * Scores and their running max/sum stay on chip: S = Q K^T is formed one
+ * key tile at a time on bf16 matrix cores with float32 accumulation, the
+ * probabilities are rounded to bf16 for the P V product, and O is divided by
+ * the running sum once, after the last tile.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Forward pass with float32 inputs, computed entirely in float32 (same
+ * contract as fa_fwd otherwise).  For small exact checks; not tuned.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: one float32 per query row for
+ * D_i = dO_i . O_i.  Returns 0 for an empty or invalid shape.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass by recomputation ("The forward pass is only half of it";
+ * "Backward can recreate tiles instead of retaining the square").
+ *   q, k, v, dout : device, bf16 [B,H,N,d]   (dout = dL/dO)
+ *   o, lse        : device, float32, as written by fa_fwd for the same inputs
+ *   dq, dk, dv    : device, float32 [B,H,N,d] -- fully overwritten
+ *   workspace     : device, >= fa_bwd_workspace_bytes(B,H,N,d) bytes; its
+ *                   contents on entry do not matter
+ * The probability tiles are rebuilt from Q, K and lse; no N x N tensor is
+ * stored.  dq is accumulated with float32 atomics, so its low bits may vary
+ * from run to run; dk and dv are deterministic.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+           const void* dout, float* dq, float* dk, float* dv, void* workspace,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Static, human-readable text for an fa_status value (never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the float64 oracle.
+
+Inputs are the seeded bf16/fp32 draws of exact_io_aware_16_amd.inputs; the
+oracle sees the exact stored values in float64.  Tolerances (floating point):
+  O:           max-abs <= 1e-2 and relative L2 <= 5e-3
+  dQ, dK, dV:  max-abs <= 2e-2 and relative L2 <= 2e-2
+  L (logsumexp, our reading, no stated bound): max-abs <= 1e-3
+The float32 path is held to the first page's own bar, 1e-5.
+"""
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_16_amd as fa
+from exact_io_aware_16_amd import inputs as I
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_REL = 1e-2, 5e-3
+G_MAX, G_REL = 2e-2, 2e-2
+L_MAX = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def errs(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = x - ref
+    if d.size == 0:
+        return 0.0, 0.0
+    nref = np.linalg.norm(ref)
+    # relative L2 is undefined for an all-zero reference (e.g. dQ with one key,
+    # where dS is exactly 0); max-abs alone decides there
+    rel = float(np.linalg.norm(d) / nref) if nref > 0 else 0.0
+    return float(np.max(np.abs(d))), rel
+
+
+def run_fwd(t, causal, scale=None):
+    q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
+    o, l = fa.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), l.cpu().numpy()
+
+
+def oracle_fwd(t, causal, scale, rows=None):
+    return oracle.attention_forward_bhnd(I.to_f64(t["q"]), I.to_f64(t["k"]), I.to_f64(t["v"]), scale, causal, rows=rows)
+
+
+def check_fwd(o, l, oref, lref, tag, omax=O_MAX, orel=O_REL, lmax=L_MAX):
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), tag
+    me, re_ = errs(o, oref)
+    le, _ = errs(l, lref)
+    say(f"{tag}: O max-abs {me:.3e} rel-L2 {re_:.3e}  L max-abs {le:.3e}")
+    assert me <= omax and re_ <= orel, tag
+    assert le <= lmax, tag
+
+
+def shape_inputs(B, H, N, d, dtype, seed, qk_std=1.0, with_do=False):
+    w = I.Workload(f"test_{B}_{H}_{N}_{d}", seed, B, H, N, d, False, dtype, qk_std=qk_std)
+    return I.make_inputs(w, with_do=with_do)
+
+
+# ------------------------------------------------------------------ small and ragged shapes, full oracle
+RAGGED_N = [1, 37, 100, 129, 1000]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", RAGGED_N)
+def test_fwd_bf16_ragged(N, d, causal):
+    t = shape_inputs(1, 2, N, d, "bf16", 100 + N + d)
+    say(f"fwd bf16 N={N} d={d} causal={causal}")
+    o, l = run_fwd(t, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(d))
+    check_fwd(o, l, oref, lref, f"bf16 N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 37, 129, 300])
+def test_fwd_f32_ragged(N, d, causal):
+    t = shape_inputs(2, 1, N, d, "f32", 200 + N + d)
+    say(f"fwd f32 N={N} d={d} causal={causal}")
+    o, l = run_fwd(t, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(d))
+    check_fwd(o, l, oref, lref, f"f32 N={N} d={d} causal={causal}", omax=1e-5, orel=1e-5, lmax=1e-5)
+
+
+def test_fwd_f32_tiny_exact_workload():
+    w = I.TINY_F32
+    t = I.make_inputs(w)
+    say(f"{w.name}")
+    o, l = run_fwd(t, w.causal)
+    oref, lref = oracle_fwd(t, w.causal, w.scale)
+    check_fwd(o, l, oref, lref, w.name, omax=1e-5, orel=1e-5, lmax=1e-5)
+
+
+# ------------------------------------------------------------------ the measured workloads
+def test_fwd_4k_d128_full():
+    w = I.FWD_4K_D128
+    t = I.make_inputs(w)
+    say(w.name)
+    o, l = run_fwd(t, w.causal)
+    oref, lref = oracle_fwd(t, w.causal, w.scale)
+    check_fwd(o, l, oref, lref, w.name)
+
+
+@pytest.mark.parametrize("w", [I.CAUSAL_8K_D64_WIDE, I.CAUSAL_32K_D128], ids=lambda w: w.name)
+def test_fwd_long_causal_sampled_rows(w):
+    """Full-size launch; the oracle evaluates 256 seeded rows of every head."""
+    t = I.make_inputs(w)
+    say(w.name)
+    o, l = run_fwd(t, w.causal)
+    rows = lambda b, h: I.sample_rows(w.N, 256, 1000 * w.case + b * w.H + h)
+    oref, lref = oracle_fwd(t, w.causal, w.scale, rows=rows)
+    og = np.stack([np.stack([o[b, h][rows(b, h)] for h in range(w.H)]) for b in range(w.B)])
+    lg = np.stack([np.stack([l[b, h][rows(b, h)] for h in range(w.H)]) for b in range(w.B)])
+    check_fwd(og, lg, oref, lref, w.name)
+
+
+# ------------------------------------------------------------------ invariants and edge cases
+def test_fwd_uniform_scores_give_mean_of_values():
+    """Q = 0: every visible key has weight 1/count (closed form)."""
+    N, d = 777, 128
+    t = shape_inputs(1, 2, N, d, "bf16", 300)
+    t["q"] = torch.zeros_like(t["q"])
+    for causal in (False, True):
+        o, l = run_fwd(t, causal)
+        v = I.to_f64(t["v"])
+        if causal:
+            ref = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+            lref = np.broadcast_to(np.log(np.arange(1, N + 1)), l.shape)
+        else:
+            ref = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+            lref = np.full(l.shape, math.log(N))
+        check_fwd(o, l, ref, lref, f"uniform causal={causal}", omax=1e-5, orel=1e-5, lmax=1e-5)
+
+
+def test_fwd_late_max_rescale():
+    """One key far above the rest, in the last tile: every earlier tile's
+    contribution must be scaled down by the rescale factor."""
+    N, d = 1000, 64
+    t = shape_inputs(1, 1, N, d, "bf16", 301)
+    q = torch.zeros(1, 1, N, d)
+    q[..., 0] = 1.0
+    k = torch.zeros(1, 1, N, d)
+    k[0, 0, :, 0] = torch.linspace(-1, 1, N)
+    k[0, 0, N - 1, 0] = 60.0  # score 60/8 = 7.5 above the others
+    t["q"], t["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    o, l = run_fwd(t, False)
+    oref, lref = oracle_fwd(t, False, 1 / math.sqrt(d))
+    check_fwd(o, l, oref, lref, "late max")
+
+
+def test_fwd_kv_permutation_invariance():
+    N, d = 333, 128
+    t = shape_inputs(1, 2, N, d, "bf16", 302)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(N))
+    o1, l1 = run_fwd(t, False)
+    t2 = dict(t, k=t["k"][:, :, perm].contiguous(), v=t["v"][:, :, perm].contiguous())
+    o2, l2 = run_fwd(t2, False)
+    me, _ = errs(o1, o2)
+    le, _ = errs(l1, l2)
+    say(f"permutation: O moves {me:.2e}, L moves {le:.2e}")
+    assert me <= 5e-3 and le <= 1e-4
+
+
+def test_fwd_scale_argument():
+    N, d = 200, 64
+    t = shape_inputs(1, 1, N, d, "bf16", 303)
+    o, l = run_fwd(t, True, scale=0.37)
+    oref, lref = oracle_fwd(t, True, 0.37)
+    check_fwd(o, l, oref, lref, "scale 0.37")
+
+
+def test_empty_problem_is_a_noop():
+    z = torch.zeros(1, 1, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o, l = fa.forward(z, z, z)
+    assert o.shape == (1, 1, 0, 64) and l.shape == (1, 1, 0)
+
+
+# ------------------------------------------------------------------ backward
+def run_bwd(t, causal):
+    q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
+    o, l = fa.forward(q, k, v, causal=causal)
+    dq, dk, dv = fa.backward(q, k, v, o, l, do, causal=causal)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def oracle_bwd(t, causal, scale):
+    return oracle.attention_backward_bhnd(*(I.to_f64(t[n]) for n in ("q", "k", "v", "do")), scale, causal)
+
+
+def check_bwd(got, ref, tag):
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref[:3]):
+        assert np.all(np.isfinite(a)), (tag, name)
+        me, re_ = errs(a, b)
+        say(f"{tag} {name}: max-abs {me:.3e} rel-L2 {re_:.3e}")
+        assert me <= G_MAX and re_ <= G_REL, (tag, name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 37, 129, 300])
+def test_bwd_ragged(N, d, causal):
+    t = shape_inputs(1, 2, N, d, "bf16", 400 + N + d, with_do=True)
+    say(f"bwd N={N} d={d} causal={causal}")
+    got = run_bwd(t, causal)
+    check_bwd(got, oracle_bwd(t, causal, 1 / math.sqrt(d)), f"bwd N={N} d={d} causal={causal}")
+
+
+def test_fwdbwd_4k_d128_causal_full():
+    w = I.FWDBWD_4K_D128
+    t = I.make_inputs(w)
+    say(w.name)
+    q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
+    o, l = fa.forward(q, k, v, causal=w.causal)
+    torch.cuda.synchronize()
+    oref, lref = oracle_fwd(t, w.causal, w.scale)
+    check_fwd(o.cpu().numpy(), l.cpu().numpy(), oref, lref, w.name + " fwd")
+    got = run_bwd(t, w.causal)
+    check_bwd(got, oracle_bwd(t, w.causal, w.scale), w.name)
