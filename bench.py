@@ -1,0 +1,233 @@
+"""Throughput of the exact-attention hot path on one MI355X.
+
+A step is one pass of the whole path -- fa_fwd then fa_bwd (D preprocess and
+the recompute backward) -- over the forward+backward workload
+B=2, H=16, N=4096, d=128, causal, bf16 Q/K/V/dO ~ N(0,1), with inputs resident
+in device memory before the timed region.  ``value`` is attention TFLOP/s of
+the step: 3.5 * (4*B*H*N^2*d / 2) FLOP per step (forward counted as
+4*B*H*N^2*d halved for causal, backward as 2.5x the forward).
+
+Also reported on the same line:
+  fwd        forward alone on B=1, H=8, N=4096, d=128, non-causal
+  phases     forward and backward of the step timed separately
+  roofline   the dominant kernel (the backward's main kernel) against the
+             bf16 matrix-core peak; traffic from committed rocprofv3 counters
+             when they were taken on the current kernel sources
+  cpu_baseline  the float64 oracle on a bounded sample of the workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2048 bf16 FMA/clk (4096 FLOP) x 2.4 GHz, dense
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def committed_traffic(kernel_key):
+    """HBM bytes per launch from profiles/traffic.json, if still current."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None, "no counter record"
+    rec = json.load(open(path))
+    entry = rec.get("kernels", {}).get(kernel_key)
+    if entry is None:
+        return None, "kernel not in counter record"
+    from exact_io_aware_16_amd.counters import kernel_source_digest
+
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None, "kernel sources changed since the counters were taken"
+    return entry["hbm_bytes_per_launch"], "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+
+
+def time_calls(fn, iters, stream):
+    """Average ms per call of fn() over iters calls, bracketed by events on the launch stream."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline(w, t, budget_s=12.0):
+    """The oracle (untuned) on whole heads of the workload until ~budget_s of work."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from exact_io_aware_16_amd.inputs import to_f64
+
+    f64 = {n: to_f64(t[n]) for n in ("q", "k", "v", "do")}
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t0 = 0, time.perf_counter()
+    for b, h in heads:
+        oracle.attention_forward(f64["q"][b, h], f64["k"][b, h], f64["v"][b, h], w.scale, w.causal)
+        oracle.attention_backward(f64["q"][b, h], f64["k"][b, h], f64["v"][b, h], f64["do"][b, h], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    flop = 3.5 * w.fwd_flop() * done / len(heads)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": flop / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} heads of the step's workload, full rows, float64 forward + backward "
+                  f"({el:.1f} s); FLOP counted as for the GPU step",
+        "seconds": el,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this attention path has no multi-GPU mode "
+              "(heads and batch shard with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_16_amd as fa
+    from exact_io_aware_16_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    # ------------------------------------------------------------ the step: fwd + bwd
+    w = I.FWDBWD_4K_D128
+    t = I.make_inputs(w)
+    q, k, v, do = (t[n].to(dev) for n in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws = torch.empty((fa.library().fa_bwd_workspace_bytes(B, H, N, d),), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        fa.forward(q, k, v, causal=True, out=o, lse=lse)
+
+    def bwd():
+        fa.backward(q, k, v, o, lse, do, causal=True, workspace=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: exactly --steps steps, synchronised on both sides
+    t_start = time.perf_counter()
+    ms_step = time_calls(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_flop = 3.5 * w.fwd_flop()
+    value = step_flop / (ms_step * 1e-3) / 1e12
+
+    ms_fwd = time_calls(fwd, args.steps, stream)
+    ms_bwd = time_calls(bwd, args.steps, stream)
+    bwd_tflops = 2.5 * w.fwd_flop() / (ms_bwd * 1e-3) / 1e12
+    traffic, traffic_src = committed_traffic("bwd_main_d128_causal")
+
+    # ------------------------------------------------------------ forward headline workload
+    wf = I.FWD_4K_D128
+    tf = I.make_inputs(wf)
+    qf, kf, vf = (tf[n].to(dev) for n in ("q", "k", "v"))
+    of = torch.empty(qf.shape, dtype=torch.float32, device=dev)
+    lf = torch.empty(qf.shape[:3], dtype=torch.float32, device=dev)
+
+    def fwd2():
+        fa.forward(qf, kf, vf, causal=False, out=of, lse=lf)
+
+    for _ in range(args.warmup):
+        fwd2()
+    ms_f2 = time_calls(fwd2, args.steps, stream)
+    f2 = wf.fwd_flop() / (ms_f2 * 1e-3) / 1e12
+    f2_traffic, f2_src = committed_traffic("fwd_d128")
+
+    res = {
+        "metric": "attention TFLOP/s (fwd, fwd+bwd) bf16 at 1 MI355X; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+            "step": "fa_fwd + fa_bwd",
+            "flop_per_step": step_flop,
+            "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "parallelism": "single GPU",
+        },
+        "phases": {
+            "fwd_ms": round(ms_fwd, 4),
+            "fwd_tflops": round(w.fwd_flop() / (ms_fwd * 1e-3) / 1e12, 2),
+            "bwd_ms": round(ms_bwd, 4),
+            "bwd_tflops": round(bwd_tflops, 2),
+        },
+        "roofline": {
+            "kernel": "bwd_main_kernel<128, causal> (timed as the fa_bwd call, which adds the small D preprocess)",
+            "bound": "mfma",
+            "achieved": round(bwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "traffic_source": traffic_src,
+            "algorithmic_flop_per_launch": 2.5 * w.fwd_flop(),
+        },
+        "fwd": {
+            "workload": wf.name,
+            "ms": round(ms_f2, 4),
+            "tflops": round(f2, 2),
+            "roofline": {
+                "kernel": "fwd_bf16_kernel<128, non-causal>",
+                "bound": "mfma",
+                "achieved": round(f2, 2),
+                "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(f2 / PEAK_BF16_TFLOPS, 4),
+                "traffic": f2_traffic,
+                "traffic_source": f2_src,
+                "algorithmic_flop_per_launch": wf.fwd_flop(),
+            },
+        },
+        "timed_wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, t)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,6 +46,18 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Operand-register reuse and the matrix core.  An issued MFMA may wait for
+// the matrix unit (behind the previous MFMA) before it reads its A/B
+// registers, and nothing stops a later load from overwriting those registers
+// in the meantime; the compiler does not guard that write-after-read.  The
+// kernels therefore rotate operand registers through two sets and keep each
+// set live until the next group of MFMAs has been issued (by which time the
+// earlier group has started), using pin(): an empty asm statement that reads
+// the operands together with the result of a later MFMA, which orders it
+// after that MFMA and extends the operands' live ranges to it.  Emits no code.
+__device__ __forceinline__ void pin(const bf16x8& v, const f32x16& after) { asm volatile("" ::"v"(v), "v"(after)); }
+__device__ __forceinline__ void pin(const bf16x8& v, float after) { asm volatile("" ::"v"(v), "v"(after)); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -59,6 +71,30 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = (__bf16)p[e];
   return r;
+}
+
+// Combine each lane with its partner in the other half of the wave (lane
+// l and l ^ 32) using v_permlane32_swap, without a trip through LDS.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + sum of the eight bf16 values, exactly as stored (v_dot2 against 1.0).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const uint4 w = __builtin_bit_cast(uint4, v);
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), one, acc, false);
+  return acc;
 }
 
 // Workgroup order: the hardware hands consecutive workgroup ids to the eight

@@ -3,26 +3,39 @@
 // Follows the blocked recurrence of "From softmax to attention: rescale the
 // output too" (FlashAttention: The Matrix You Never Have to Write Down):
 // per query row a running max m, running sum l and unnormalised output O;
-// each key tile raises m to m_new, scales l and O by e^(m - m_new), adds the
-// tile's terms, and O is divided by l once after the last tile.  The scores
-// never leave the chip.
+// a key tile whose scores exceed m moves the reference to m_new and scales
+// l and O by e^(m - m_new); the tile's terms are added; O is divided by l
+// once after the last tile.  Scores never leave the chip.
+//
+// Rescale policy: the reference m only moves when a tile's row max exceeds
+// it by more than kRescaleSlack (log2 units) for some row of the wave, as in
+// the deferred correction described under "What it doesn't solve" (FA4
+// paragraph) of the same page.  Until then the tile's exponentials are taken
+// against the old reference (values up to 2^kRescaleSlack), l and O stay in
+// one consistent frame, and the final O / l and L = m + log l are the same
+// function -- only the rounding differs.
 //
 // Work split (one workgroup = 4 waves = 128 query rows of one head):
 //  * each wave owns 32 query rows; its Q block stays in registers for the
 //    whole kernel as the B operand of S^T = K Q^T (keys along M, queries
 //    along N), so a query's scores sit in one lane pair (lanes c, c+32) and
-//    the row max needs a single cross-half exchange;
-//  * key/value tiles of BC rows are staged through LDS, double buffered:
-//    K row-major (rows loaded in perm32 order, see fa_common.h), V
-//    transposed (V^T[d][key]) so both products read 16-byte operand runs;
-//  * P is rounded to bf16 in registers and used directly as the B operand of
-//    O^T += V^T P^T -- the perm32 key order makes the S result layout equal
-//    to the operand layout, so P never touches LDS;
-//  * scores are scaled by scale*log2(e) and exponentiated with v_exp_f32
-//    (base 2); L is converted back to natural log in the epilogue.
-//  * causal: query block qb visits key tiles up to its diagonal only; waves
-//    whose rows all precede a tile skip its arithmetic; element masks are
-//    applied only on tiles that straddle the diagonal or the ragged end.
+//    the row max needs one cross-half exchange;
+//  * K and V tiles (BC keys) are copied global -> LDS directly
+//    (global_load_lds, 16 bytes per lane, no register staging), double
+//    buffered, with a 16-byte-slot XOR swizzle instead of padding:
+//      K: row r holds key perm32(r), slot (chunk ^ (r & 7))
+//      V: row r holds key r,         slot (chunk ^ 2*(r & 3))
+//    so operand reads are bank-conflict free;
+//  * V stays row-major: the O^T += V^T P^T operand is read with
+//    ds_read_b64_tr_b16, which hands each lane 4 consecutive keys of one
+//    head-dimension column;
+//  * P is rounded to bf16 in registers and used directly as the B operand
+//    (the perm32 key order makes the S result layout equal to the operand
+//    layout);
+//  * software pipelined: while the softmax of tile t runs on the vector ALU,
+//    the matrix cores already compute S for tile t+1;
+//  * causal: query block qb visits key tiles up to its diagonal only, masks
+//    are applied only on tiles that straddle the diagonal or the ragged end.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -31,77 +44,111 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBR = 32 * kWaves;  // query rows per workgroup
+constexpr int kBR = 32 * kWaves;        // query rows per workgroup
+constexpr float kRescaleSlack = 8.0f;   // log2 units: P <= 256 before a forced rescale
 
 template <int D> struct FwdTile;
 template <> struct FwdTile<128> { static constexpr int BC = 64; };
 template <> struct FwdTile<64> { static constexpr int BC = 128; };
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
 template <int D>
 struct FwdSmem {
   static constexpr int BC = FwdTile<D>::BC;
-  static constexpr int KLD = D + 8;   // K row stride (elements); 16-byte pad
-  static constexpr int VLD = BC + 8;  // V^T row stride (elements)
-  bf16_raw k[2][BC * KLD];
-  bf16_raw vt[2][D * VLD];
+  bf16_raw k[2][BC * D];
+  bf16_raw v[2][BC * D];
 };
 
-// Per-thread staging of one K/V tile between the global load and the LDS store.
+// LDS tile layout.  Each BC x D bf16 tile is stored densely, row by row,
+// in 16-byte slots; a slot's position is XOR-swizzled so that the operand
+// reads hit 64 distinct banks per 16-lane phase (rows of 256 B span the whole
+// bank width for d = 128, rows of 128 B span half of it for d = 64):
+//   K tile: row r holds key perm32(r) (within each 32-row group), chunk c of
+//           the row sits in slot c ^ kswz(r)
+//   V tile: row r holds key r, chunk c sits in slot c ^ vswz(r)
 template <int D>
-struct TileRegs {
-  static constexpr int BC = FwdTile<D>::BC;
-  static constexpr int KCH = BC * D / 8 / kThreads;  // 16-byte K chunks per thread (4)
-  uint4 k[KCH];
-  uint4 v[4];  // 4 consecutive key rows x 8 d of V
-};
-
+__device__ __forceinline__ constexpr int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const bf16_raw* __restrict__ Kh,
-                                          const bf16_raw* __restrict__ Vh, int key0, int N, int tid) {
-  constexpr int BC = FwdTile<D>::BC;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-#pragma unroll
-  for (int j = 0; j < TileRegs<D>::KCH; ++j) {
-    const int ch = j * kThreads + tid;
-    const int row = ch / CPR, col = (ch % CPR) * 8;
-    const int key = key0 + row;
-    r.k[j] = key < N ? ld16(Kh + (size_t)key * D + col) : make_uint4(0, 0, 0, 0);
-  }
-  const int kb4 = tid % (BC / 4), d8 = tid / (BC / 4);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int key = key0 + 4 * kb4 + j;
-    r.v[j] = key < N ? ld16(Vh + (size_t)key * D + 8 * d8) : make_uint4(0, 0, 0, 0);
-  }
+__device__ __forceinline__ constexpr int vswz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
+// Per-lane byte offsets of the 16-byte chunks one thread copies for a tile
+// (relative to the tile's first key).  The copy is an LDS-direct buffer load:
+// lane l of an instruction writes LDS bytes [m0 + 16 l, m0 + 16 l + 16), so
+// the swizzle is applied on the source side, and offsets past the end of the
+// head (the ragged last tile) read as zeros.
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, FwdSmem<D>& sm, int buf, int tid) {
-  constexpr int BC = FwdTile<D>::BC;
-  constexpr int CPR = D / 8;
-  constexpr int KLD = FwdSmem<D>::KLD, VLD = FwdSmem<D>::VLD;
+struct TileCopy {
+  static constexpr int BC = FwdTile<D>::BC;
+  static constexpr int SLOTS = D / 8;
+  static constexpr int ROWS_PER_INSTR = 64 / SLOTS;
+  static constexpr int INSTR = BC * SLOTS / kThreads;
+  uint32_t k_off[INSTR], v_off[INSTR];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::KCH; ++j) {
-    const int ch = j * kThreads + tid;
-    const int row = ch / CPR, col = (ch % CPR) * 8;
-    const int lrow = (row & ~31) | perm32(row & 31);
-    st16(&sm.k[buf][lrow * KLD + col], r.k[j]);
+    for (int i = 0; i < INSTR; ++i) {
+      const int blk = i * kWaves + wave;
+      const int r = blk * ROWS_PER_INSTR + lane / SLOTS;
+      const int slot = lane % SLOTS;
+      k_off[i] = (uint32_t)(((r & ~31) + perm32(r & 31)) * D * 2 + 16 * (slot ^ kswz<D>(r)));
+      v_off[i] = (uint32_t)(r * D * 2 + 16 * (slot ^ vswz<D>(r)));
+    }
   }
-  // transpose 4 keys x 8 d into 8 rows of V^T, 4 keys (8 bytes) each
-  const int kb4 = tid % (BC / 4), d8 = tid / (BC / 4);
-  const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&r.v[0]);
-  const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&r.v[1]);
-  const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&r.v[2]);
-  const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&r.v[3]);
+};
+
+// One 16-byte-per-lane LDS-direct load.  Issued as inline assembly so that
+// the compiler does not serialise every later LDS read behind it (it cannot
+// tell which LDS bytes the copy writes); completion is awaited explicitly
+// with wait_tile_loads() before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                           uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+               : "memory");
+}
+__device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int D, bool IS_K>
+__device__ __forceinline__ void issue_tile(bf16_raw* lds_tile, __amdgpu_buffer_rsrc_t rsrc, int key0,
+                                           const TileCopy<D>& tc, int wave) {
+  const uint32_t soff = (uint32_t)key0 * D * 2;
+  const uint32_t base = lds_addr_of(lds_tile);
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint2 lo, hi;  // d = 8*d8 + 2w (low halves) and 2w+1 (high halves)
-    lo.x = (v0[w] & 0xffffu) | (v1[w] << 16);
-    lo.y = (v2[w] & 0xffffu) | (v3[w] << 16);
-    hi.x = (v0[w] >> 16) | (v1[w] & 0xffff0000u);
-    hi.y = (v2[w] >> 16) | (v3[w] & 0xffff0000u);
-    *reinterpret_cast<uint2*>(&sm.vt[buf][(8 * d8 + 2 * w) * VLD + 4 * kb4]) = lo;
-    *reinterpret_cast<uint2*>(&sm.vt[buf][(8 * d8 + 2 * w + 1) * VLD + 4 * kb4]) = hi;
+  for (int i = 0; i < TileCopy<D>::INSTR; ++i)
+    lds_copy16(rsrc, IS_K ? tc.k_off[i] : tc.v_off[i], soff, base + (uint32_t)(i * kWaves + wave) * 1024u);
+}
+
+// S^T (BC keys x 32 queries) = K Q^T from one LDS K tile.  kaddr[kk] is the
+// lane's byte offset of its 16-byte operand for head-dim slice kk in key
+// block 0; key block kb adds the constant 32 * kb rows.  K operands rotate
+// through the two sets of ak (see pin()); the set used last stays live for
+// the caller to release once the scores have been consumed.
+template <int D>
+__device__ __forceinline__ void tile_scores(f32x16 (&s)[FwdTile<D>::BC / 32], const char* ktile,
+                                            const int (&kaddr)[D / 16], const bf16x8 (&qf)[D / 16],
+                                            bf16x8 (&ak)[2][FwdTile<D>::BC / 32]) {
+  constexpr int NKB = FwdTile<D>::BC / 32;
+  constexpr int NKK = D / 16;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    bf16x8 (&a)[NKB] = ak[kk & 1];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) a[kb] = as_bf16x8(ld16(ktile + kaddr[kk] + kb * 32 * D * 2));
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(a[kb], qf[kk], kk == 0 ? f32x16{} : s[kb]);
+    // the other set (group kk-1) may be overwritten from here on
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) pin(ak[(kk + 1) & 1][kb], s[NKB - 1]);
   }
 }
 
@@ -113,7 +160,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NKK = D / 16;    // 16-wide slices of the head dimension
   constexpr int NDB = D / 32;    // 32-row blocks of O^T
-  constexpr int KLD = FwdSmem<D>::KLD, VLD = FwdSmem<D>::VLD;
   __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
 
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -132,112 +178,166 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int q_start = qb * kBR;
   const int q0w = q_start + 32 * wave;
   const int my_q = q0w + col;
-  const bool wave_live = q0w < N;
-
-  bf16x8 qf[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-    qf[kk] = as_bf16x8(my_q < N ? ld16(Qh + (size_t)my_q * D + 16 * kk + 8 * g) : make_uint4(0, 0, 0, 0));
 
   const int kv_end = CAUSAL ? min(N, q_start + kBR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
-  TileRegs<D> tr;
-  load_tile<D>(tr, Kh, Vh, 0, N, tid);
-  store_tile<D>(tr, sm, 0, tid);
-  __syncthreads();
+  TileCopy<D> tc;
+  tc.init(wave, lane);
+  // per-head buffer descriptors: reads past the head's last key return 0
+  const int head_bytes = N * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, head_bytes, 0x00020000);
+  // prologue loads: K(0), V(0)
+  issue_tile<D, true>(sm.k[0], krs, 0, tc, wave);
+  issue_tile<D, false>(sm.v[0], vrs, 0, tc, wave);
+
+  // loop-invariant lane parts of the LDS operand addresses (bytes)
+  int kaddr[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) kaddr[kk] = col * D * 2 + 16 * ((2 * kk + g) ^ kswz<D>(col));
+  const int grp = lane >> 4, sl = lane & 15;
+  int vaddr[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int kr = 8 * (grp >> 1) + (sl >> 2);  // row within a 16-row slice (plus constants)
+    const int d = 32 * db + 16 * (grp & 1) + 4 * (sl & 3);
+    vaddr[db] = kr * D * 2 + 16 * ((d >> 3) ^ vswz<D>(kr)) + 2 * (d & 7);
+  }
+
+  bf16x8 qf[NKK];
+  {
+    const int qr = min(my_q, N - 1);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(ld16(Qh + (size_t)qr * D + 16 * kk + 8 * g));
+  }
 
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f, l_rnd = 0.f;
 
+  // operand register sets (see pin()): K operands of the score product and
+  // V^T operands of the P V product, two sets each
+  bf16x8 ak[2][NKB], av[2][NDB], pb[NKB][2];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) pb[kb][0] = pb[kb][1] = bf16x8{};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) ak[j][kb] = bf16x8{};
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) av[j][db] = bf16x8{};
+  }
+
+  f32x16 s_cur[NKB];
   for (int t = 0; t < n_tiles; ++t) {
     const int key0 = t * BC;
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile<D>(tr, Kh, Vh, key0 + BC, N, tid);
-
-    const bool active = wave_live && (!CAUSAL || key0 <= q0w + 31);
-    if (active) {
-      // S^T = K Q^T for this tile: NKB blocks of 32 keys x 32 queries
-      f32x16 s[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const bf16x8 a = as_bf16x8(ld16(&sm.k[buf][(32 * kb + col) * KLD + 16 * kk + 8 * g]));
-          s[kb] = mfma32(a, qf[kk], s[kb]);
-        }
-      }
-      const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > N;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 32 * kb + perm_row(i, g);
-            if (key >= N || (CAUSAL && key > my_q)) s[kb][i] = -INFINITY;
-          }
-      }
-      // online softmax: running max over this tile (both lane halves)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // row with nothing visible yet
-      const float alpha = fast_exp2(m_run - m_use);           // 0 on the first visible tile
-      m_run = m_new;
-
-      bf16x8 pb[NKB][2];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = fast_exp2(fmaf(s[kb][8 * h + e], c, -m_use));
-            rs += p[e];
-          }
-          pb[kb][h] = pack_bf16x8(p);
-        }
-      l_run = l_run * alpha + rs;  // this lane's half of the row sum
-
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8 a = as_bf16x8(ld16(&sm.vt[buf][(32 * db + col) * VLD + 32 * kb + 16 * h + 8 * g]));
-            oacc[db] = mfma32(a, pb[kb][h], oacc[db]);
-          }
-    }
-    if (t + 1 < n_tiles) store_tile<D>(tr, sm, buf ^ 1, tid);
+    // K(t) and V(t) have landed (own loads) and are visible (barrier); every
+    // wave is done with tile t-1, whose buffers refill now with tile t+1.
+    wait_tile_loads();
     __syncthreads();
+    if (t + 1 < n_tiles) {
+      issue_tile<D, true>(sm.k[(t + 1) & 1], krs, key0 + BC, tc, wave);
+      issue_tile<D, false>(sm.v[(t + 1) & 1], vrs, key0 + BC, tc, wave);
+    }
+    tile_scores<D>(s_cur, reinterpret_cast<const char*>(sm.k[t & 1]), kaddr, qf, ak);
+
+    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > N;
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * kb + perm_row(i, g);
+          if (key >= N || (CAUSAL && key > my_q)) s_cur[kb][i] = -INFINITY;
+        }
+    }
+    // tile row max (both lane halves), in log2 units
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
+    mx = halves_max(mx) * c;
+    // the scores of tile t are consumed: every MFMA issued before the row max
+    // (all K and V^T operand sets of this and the previous tile) has run
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) pin(ak[j][kb], mx);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) pin(av[j][db], mx);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      pin(pb[kb][0], mx);
+      pin(pb[kb][1], mx);
+    }
+    if (__any(mx > m_ref + kRescaleSlack)) {
+      const float m_new = fmaxf(m_ref, mx);
+      // 0 while nothing was accumulated; a row with nothing visible keeps its (zero) sums
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+      l_rnd *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;  // row with nothing visible yet
+
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(s_cur[kb][8 * h + e], c, -m_use));
+          l_run += p[e];
+        }
+        pb[kb][h] = pack_bf16x8(p);
+        // l_rnd sums the bf16-rounded weights that actually multiply V, so O
+        // is normalised by exactly the weights applied (a dominant weight's
+        // rounding cancels in O / l_rnd); l_run (exact terms) gives L.
+        l_rnd = sum_bf16x8(pb[kb][h], l_rnd);
+      }
+
+    // O^T += V^T P^T, V^T operand via transpose reads of the row-major tile;
+    // operand sets rotate per (key block, half) group
+    const char* vtile = reinterpret_cast<const char*>(sm.v[t & 1]);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int grp_i = 2 * kb + h;
+        bf16x8 (&a)[NDB] = av[grp_i & 1];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          v4i16 part[2];
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr)
+            part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(vtile + vaddr[db] + (32 * kb + 16 * h + 4 * rr) * D * 2));
+          a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(a[db], pb[kb][h], oacc[db]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) pin(av[(grp_i + 1) & 1][db], oacc[NDB - 1]);
+        if (grp_i > 0) pin(pb[(grp_i - 1) >> 1][(grp_i - 1) & 1], oacc[NDB - 1]);
+      }
   }
 
   // epilogue: combine the two half-row sums, normalise once, write O and L
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = halves_sum(l_run);
+  const float l_nrm = halves_sum(l_rnd);
   if (my_q < N) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_nrm > 0.f ? 1.f / l_nrm : 0.f;
     float* Orow = O + head + (size_t)my_q * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -250,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         v.w = oacc[db][4 * i4 + 3] * inv;
         *reinterpret_cast<float4*>(Orow + 32 * db + 8 * i4 + 4 * g) = v;
       }
-    if (g == 0) LSE[(size_t)bh * N + my_q] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (g == 0) LSE[(size_t)bh * N + my_q] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
