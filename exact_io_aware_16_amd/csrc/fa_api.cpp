@@ -59,7 +59,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   bool empty = false;
   if (check_shape(B, H, N, d, 0, &empty) != FA_OK || empty) return 0;
-  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  return 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,

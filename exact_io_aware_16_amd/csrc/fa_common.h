@@ -50,12 +50,16 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // the matrix unit (behind the previous MFMA) before it reads its A/B
 // registers, and nothing stops a later load from overwriting those registers
 // in the meantime; the compiler does not guard that write-after-read.  The
-// kernels therefore rotate operand registers through two sets and keep each
-// set live until the next group of MFMAs has been issued (by which time the
-// earlier group has started), using pin(): an empty asm statement that reads
-// the operands together with the result of a later MFMA, which orders it
-// after that MFMA and extends the operands' live ranges to it.  Emits no code.
-__device__ __forceinline__ void pin(const bf16x8& v, const f32x16& after) { asm volatile("" ::"v"(v), "v"(after)); }
+// kernels therefore rotate operand registers through two sets and release a
+// set only after the next group of MFMAs has been issued:
+//   group_fence()  -- no instruction is scheduled across it, so every MFMA of
+//                     the group before it is issued before anything after it;
+//   pin(v)         -- empty asm reading v: keeps v's registers live (and not
+//                     reused) up to this point.  Emits no code.
+// At the end of a phase, pin(v, x) with x computed from all of the phase's
+// MFMA results keeps the operands live until those MFMAs have completed.
+__device__ __forceinline__ void group_fence() { __builtin_amdgcn_sched_barrier(0); }
+__device__ __forceinline__ void pin(const bf16x8& v) { asm volatile("" ::"v"(v)); }
 __device__ __forceinline__ void pin(const bf16x8& v, float after) { asm volatile("" ::"v"(v), "v"(after)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

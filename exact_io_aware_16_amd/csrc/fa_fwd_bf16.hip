@@ -82,7 +82,8 @@ __device__ __forceinline__ constexpr int vswz(int r) {
 // (relative to the tile's first key).  The copy is an LDS-direct buffer load:
 // lane l of an instruction writes LDS bytes [m0 + 16 l, m0 + 16 l + 16), so
 // the swizzle is applied on the source side, and offsets past the end of the
-// head (the ragged last tile) read as zeros.
+// head (the ragged last tile) read as zeros -- nothing outside the head is
+// ever read.
 template <int D>
 struct TileCopy {
   static constexpr int BC = FwdTile<D>::BC;
@@ -118,14 +119,16 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// The tile offset is added to the per-lane offset, which the hardware range
+// checks against the head's size; the scalar offset stays 0.
 template <int D, bool IS_K>
 __device__ __forceinline__ void issue_tile(bf16_raw* lds_tile, __amdgpu_buffer_rsrc_t rsrc, int key0,
                                            const TileCopy<D>& tc, int wave) {
-  const uint32_t soff = (uint32_t)key0 * D * 2;
+  const uint32_t toff = (uint32_t)key0 * D * 2;
   const uint32_t base = lds_addr_of(lds_tile);
 #pragma unroll
   for (int i = 0; i < TileCopy<D>::INSTR; ++i)
-    lds_copy16(rsrc, IS_K ? tc.k_off[i] : tc.v_off[i], soff, base + (uint32_t)(i * kWaves + wave) * 1024u);
+    lds_copy16(rsrc, (IS_K ? tc.k_off[i] : tc.v_off[i]) + toff, 0u, base + (uint32_t)(i * kWaves + wave) * 1024u);
 }
 
 // S^T (BC keys x 32 queries) = K Q^T from one LDS K tile.  kaddr[kk] is the
@@ -146,9 +149,10 @@ __device__ __forceinline__ void tile_scores(f32x16 (&s)[FwdTile<D>::BC / 32], co
     for (int kb = 0; kb < NKB; ++kb) a[kb] = as_bf16x8(ld16(ktile + kaddr[kk] + kb * 32 * D * 2));
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(a[kb], qf[kk], kk == 0 ? f32x16{} : s[kb]);
-    // the other set (group kk-1) may be overwritten from here on
+    // group kk is issued: the other set (group kk-1) may be overwritten from here on
+    group_fence();
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) pin(ak[(kk + 1) & 1][kb], s[NKB - 1]);
+    for (int kb = 0; kb < NKB; ++kb) pin(ak[(kk + 1) & 1][kb]);
   }
 }
 
@@ -327,9 +331,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(a[db], pb[kb][h], oacc[db]);
+        group_fence();
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) pin(av[(grp_i + 1) & 1][db], oacc[NDB - 1]);
-        if (grp_i > 0) pin(pb[(grp_i - 1) >> 1][(grp_i - 1) & 1], oacc[NDB - 1]);
+        for (int db = 0; db < NDB; ++db) pin(av[(grp_i + 1) & 1][db]);
+        if (grp_i > 0) pin(pb[(grp_i - 1) >> 1][(grp_i - 1) & 1]);
       }
   }
 

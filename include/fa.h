@@ -78,8 +78,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: one float32 per query row for
- * D_i = dO_i . O_i.  Returns 0 for an empty or invalid shape.
+ * Bytes of device workspace fa_bwd needs: two float32 per query row
+ * (D_i = dO_i . O_i and L_i log2(e)).  Returns 0 for an empty or invalid
+ * shape.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
