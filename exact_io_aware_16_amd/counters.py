@@ -60,7 +60,7 @@ def kernel_key(name):
     m = re.search(r"fwd_f32_kernel(?:ILi|<)(\d+)", name)
     if m:
         return f"fwd_f32_d{m.group(1)}"
-    if "copy" in name.lower() or "elementwise" in name.lower():
+    if "copy" in name.lower():
         return "copy"
     return None
 
@@ -158,7 +158,86 @@ def summarize(args):
         rec["kernel_stats"] = _read_stats(args.stats)
     os.makedirs(args.out, exist_ok=True)
     json.dump(rec, open(os.path.join(args.out, "traffic.json"), "w"), indent=1, sort_keys=True)
+    with open(os.path.join(args.out, "counters_attention_kernels.md"), "w") as f:
+        f.write(markdown_counters(rec, args))
+    if args.stats:
+        with open(os.path.join(args.out, "kernel_trace_bench_step_and_fwd.md"), "w") as f:
+            f.write(markdown_stats(rec["kernel_stats"], args))
     print(json.dumps(rec, indent=1, sort_keys=True))
+
+
+ALGORITHMIC = {
+    # key: (workload, algorithmic HBM bytes per launch, algorithmic FLOP per launch)
+    "fwd_d128": ("B=1 H=8 N=4096 d=128 non-causal", 3 * 8 * 4096 * 128 * 2 + 8 * 4096 * 128 * 4 + 8 * 4096 * 4,
+                 4.0 * 8 * 4096 ** 2 * 128),
+    "fwd_d128_causal": ("B=2 H=16 N=4096 d=128 causal", 3 * 32 * 4096 * 128 * 2 + 32 * 4096 * 128 * 4 + 32 * 4096 * 4,
+                        2.0 * 32 * 4096 ** 2 * 128),
+    "bwd_pre_d128": ("B=2 H=16 N=4096 d=128", 32 * 4096 * 128 * (2 + 4 + 4) + 32 * 4096 * 4 * 3, 0.0),
+    "bwd_main_d128_causal": ("B=2 H=16 N=4096 d=128 causal",
+                             4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 3 * 32 * 4096 * 128 * 4,
+                             2.5 * 2.0 * 32 * 4096 ** 2 * 128),
+}
+
+
+def markdown_counters(rec, args):
+    cal = rec["calibration"]
+    out = ["# Hardware counters of the attention kernels (MI355X)", "",
+           "Collected with the committed driver `exact_io_aware_16_amd/counters.py` (5 launches of each",
+           "kernel on the forward workload B=1,H=8,N=4096,d=128 and the forward+backward workload",
+           "B=2,H=16,N=4096,d=128 causal, plus a 512 MiB device copy for calibration), one counter group",
+           "per run:", "", "```",
+           "cd /tmp && export TMPDIR=/tmp PYTHONPATH=$REPO",
+           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o run -- python -u -m exact_io_aware_16_amd.counters run",
+           "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o run -- python -u -m exact_io_aware_16_amd.counters run",
+           "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES "
+           "SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU --output-format csv -d $OUT/pmc_sq -o run -- python -u -m exact_io_aware_16_amd.counters run",
+           "python -m exact_io_aware_16_amd.counters summarize --fetch $OUT/pmc_fetch --write $OUT/pmc_write --sq $OUT/pmc_sq --stats $OUT/prof_stats",
+           "```", "",
+           f"Kernel-source digest: `{rec['source_sha256'][:16]}`.", "",
+           "## HBM traffic per launch", "",
+           f"Calibration: the 512 MiB copy reads FETCH_SIZE = {cal['fetch_kib_raw']:.0f} KiB and WRITE_SIZE = "
+           f"{cal['write_kib_raw']:.0f} KiB, so the factors are {cal['fetch_factor']:.3f} (fetch) and "
+           f"{cal['write_factor']:.3f} (write).", "",
+           "| kernel | workload | fetch MiB | write MiB | HBM MiB | algorithmic MiB | ratio |",
+           "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(rec["kernels"].items()):
+        wl, alg, _ = ALGORITHMIC.get(k, ("", 0, 0))
+        ratio = f"{v['hbm_bytes_per_launch'] / alg:.2f}" if alg else ""
+        out.append(f"| {k} | {wl} | {v['fetch_bytes'] / 2**20:.1f} | {v['write_bytes'] / 2**20:.1f} | "
+                   f"{v['hbm_bytes_per_launch'] / 2**20:.1f} | {alg / 2**20:.1f} | {ratio} |")
+    if rec.get("sq"):
+        out += ["", "## SQ counters per launch (raw sums over the device)", ""]
+        names = sorted({n for d in rec["sq"].values() for n in d})
+        out.append("| kernel | " + " | ".join(names) + " |")
+        out.append("|---|" + "---|" * len(names))
+        for k, d in sorted(rec["sq"].items()):
+            if k == "copy":
+                continue
+            out.append(f"| {k} | " + " | ".join(f"{d.get(n, 0):.0f}" for n in names) + " |")
+        out += ["", "SQ_VALU_MFMA_BUSY_CYCLES counts 32 per 32x32x16 bf16 MFMA summed over all SIMDs;",
+                "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE is the fraction of LDS cycles lost to conflicts."]
+    out.append("")
+    return "\n".join(out)
+
+
+def markdown_stats(stats, args):
+    out = ["# Kernel trace of the bench command (MI355X)", "",
+           "```",
+           "cd /tmp && export TMPDIR=/tmp",
+           "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_stats -o run -- "
+           "python -u $REPO/bench.py --no-cpu-baseline --steps 20 --warmup 5",
+           "```", "",
+           "The bench runs the fwd+bwd step (B=2,H=16,N=4096,d=128 causal), then forward and backward",
+           "alone on the same inputs, then the forward workload B=1,H=8,N=4096,d=128.", "",
+           "| kernel | calls | average us | min us | max us | TFLOP/s at average |",
+           "|---|---|---|---|---|---|"]
+    for k, v in sorted(stats.items()):
+        flop = ALGORITHMIC.get(k, ("", 0, 0))[2]
+        tf = f"{flop / (v['avg_ns'] * 1e-9) / 1e12:.1f}" if flop else ""
+        out.append(f"| {k} | {v['calls']} | {v['avg_ns'] / 1e3:.1f} | {v['min_ns'] / 1e3:.1f} | "
+                   f"{v['max_ns'] / 1e3:.1f} | {tf} |")
+    out.append("")
+    return "\n".join(out)
 
 
 def main(argv=None):
