@@ -23,6 +23,9 @@ int check_shape(int B, int H, int N, int d, int causal, bool* empty) {
   const long long bh = (long long)B * H;
   if (bh > INT32_MAX) return FA_ERR_SHAPE;
   if ((double)bh * N * d > 4.0e18) return FA_ERR_SHAPE;
+  // one head of a float32 [N,d] tensor is addressed through a buffer
+  // descriptor with 32-bit byte offsets
+  if ((long long)N * d * 4 > INT32_MAX) return FA_ERR_SHAPE;
   return FA_OK;
 }
 

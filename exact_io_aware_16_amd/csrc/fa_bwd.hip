@@ -9,41 +9,50 @@
 //   P = exp(scale S - L),  dV = P^T dO,  dP = dO V^T,
 //   D_i = sum_j P_ij dP_ij = dO_i . O_i,  dS = P * (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q.
+// The factor `scale` is folded into dS once: the kernels form
+//   dS' = scale dS = P * (scale dP - scale D)
+// (scale D comes from the preprocess), so dK = dS'^T Q and dQ = dS' K.
 //
-// Kernels:
-//  * bwd_pre_kernel: per query row D_i = dO_i . O_i and L_i log2(e) into the
-//    workspace, and dQ := 0.
-//  * bwd_main_kernel: one workgroup per (head, block of 128 keys).  Each of
-//    its 4 waves owns 32 keys: their K and V rows stay in registers (B
-//    operands of S = Q K^T and dP = dO V^T, keys along N), and dK^T, dV^T
-//    accumulate in registers.  The workgroup walks the query rows 64 at a
-//    time (causal: from the block's diagonal on).  Per query tile:
-//      - Q and dO tiles arrive by LDS-direct buffer loads (double buffered);
-//        their rows sit in perm32 order so that S and dP come out with 8
-//        consecutive query rows per register octet -- the B-operand layout
-//        of dV^T = dO^T P and dK^T = Q^T dS, whose A operands (dO^T, Q^T)
-//        are read from the same row-major tiles with ds_read_b64_tr_b16;
-//      - dS goes to LDS transposed (dS^T, one 16-byte store per octet) and
-//        is read back, again with transpose reads, as the A operand of
-//        dQ = dS K; K^T comes from the block's K tile in LDS the same way;
-//      - dQ partial sums are added to global memory with float32 atomics.
+// Kernels (three launches, no atomics, every output written once):
+//  * bwd_pre_kernel: per query row scale * (dO_i . O_i) and L_i log2(e) into
+//    the workspace.
+//  * bwd_dkdv_kernel: one workgroup per (head, block of 128 keys).  Each of
+//    its 4 waves owns 32 keys: their V rows stay in registers (B operands of
+//    dP = dO V^T), their K rows come from the block's K tile in LDS (B
+//    operands of S = Q K^T), and dK^T, dV^T accumulate in registers.  The
+//    workgroup walks the query rows 64 at a time (causal: from the block's
+//    diagonal on).  Per step:
+//      A. S and dP for the 64 rows of the tile (Q and dO tiles arrive by
+//         LDS-direct buffer loads, double buffered, rows in perm32 order so
+//         that S and dP come out with 8 consecutive query rows per register
+//         octet -- the B-operand layout of dV^T = dO^T P and dK^T = Q^T dS');
+//      B. P and dS' on the vector ALUs;
+//      C. dV^T += dO^T P and dK^T += Q^T dS', the A operands read from the
+//         row-major tiles with ds_read_b64_tr_b16.
+//    One barrier per step publishes the tile and frees the buffer the step
+//    refills.
+//  * bwd_dq_kernel (fa_bwd_dq.hip): query-stationary, recomputes S and dP
+//    per key tile and accumulates dQ in registers.
+// dQ is not accumulated across key blocks with atomics: on this part
+// device-scope float atomics are performed at the memory side, and the
+// partial sums of every key block would cross the fabric once each; the
+// second recomputation of S and dP costs less.
 //  One 16-byte-slot XOR swizzle per row width serves both the row reads and
-//  the transpose reads of a tile without LDS bank conflicts.
+//  the transpose reads of a tile without LDS bank conflicts; every per-lane
+//  LDS address is a lane constant XOR a compile-time mask, plus an
+//  immediate.
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_lds.h"
 
 namespace fa {
 namespace {
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
 // ----------------------------------------------------------------------------------- preprocess
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_raw* __restrict__ dO, const float* __restrict__ O,
-                                                       const float* __restrict__ LSE, float* __restrict__ Dvec,
-                                                       float* __restrict__ L2, float* __restrict__ dQ,
-                                                       long long rows) {
+                                                       const float* __restrict__ LSE, float* __restrict__ Dsc,
+                                                       float* __restrict__ L2, long long rows, float scale) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
   const int tid = threadIdx.x;
@@ -62,14 +71,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_raw* __restrict
       acc = fmaf(__uint_as_float(w[e] << 16), ov[2 * e], acc);
       acc = fmaf(__uint_as_float(w[e] & 0xffff0000u), ov[2 * e + 1], acc);
     }
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(dQ + off) = z;
-    *reinterpret_cast<float4*>(dQ + off + 4) = z;
   }
 #pragma unroll
   for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
   if (row < rows && part == 0) {
-    Dvec[row] = acc;
+    Dsc[row] = scale * acc;
     L2[row] = LSE[row] * kLog2e;
   }
 }
@@ -80,39 +86,14 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBKV = 32 * kWaves;  // keys per workgroup
 constexpr int kBQ = 64;            // query rows per step
 
-// Slot swizzle for tiles read both row-wise (16 consecutive rows, one 16-byte
-// slot each) and by transpose reads (4 consecutive rows x 4 slots): the
-// 16-byte slot of chunk c in row r is c ^ swz(r).
-template <int ROW_BYTES>
-__device__ __forceinline__ constexpr int swz(int r) {
-  return ROW_BYTES == 256 ? (4 * (r & 3) | ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) | ((r >> 2) & 3));
-}
-template <int ROW_BYTES>
-__device__ __forceinline__ constexpr int slot_off(int r, int chunk) {
-  return r * ROW_BYTES + 16 * (chunk ^ swz<ROW_BYTES>(r));
-}
-
 template <int D>
-struct BwdSmem {
-  bf16_raw k[kBKV * D];        // K block, rows in key order
-  bf16_raw v[kBKV * D];        // V block, rows in key order
-  bf16_raw q[2][kBQ * D];      // Q tiles, rows in perm32 order
-  bf16_raw dout[2][kBQ * D];   // dO tiles, rows in perm32 order
-  bf16_raw dst[kBKV * kBQ];    // dS^T: row = key, columns = query rows
-  float l2[2][kBQ];
-  float dv[2][kBQ];
+struct DkdvSmem {
+  bf16_raw k[kBKV * D];          // K block, rows in key order
+  bf16_raw q[2][kBQ * D];        // Q tiles, rows in perm32 order
+  bf16_raw dout[2][kBQ * D];     // dO tiles, rows in perm32 order
+  float l2[2][kBQ];              // L log2(e) of the tile's rows
+  float dsc[2][kBQ];             // scale * D of the tile's rows
 };
-
-__device__ __forceinline__ void lds_copy(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // 16-byte chunks a thread copies for one BQ x D query tile: LDS block
 // (i*4 + wave) of 1 KiB, lane l -> row r, slot s; the source is row
@@ -133,25 +114,18 @@ struct QCopy {
   }
 };
 
-// A transpose read: four bf16 of one column, 4 consecutive rows; two of them
-// make the 8-element operand.
-__device__ __forceinline__ bf16x8 tr_pair(const char* base, int off0, int off1) {
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + off0));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + off1));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
-    const bf16_raw* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
-    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int N, int n_kvblk, int total,
-    float scale, float c) {
-  constexpr int NKK = D / 16;           // 16-wide head-dim slices (contraction of S and dP)
-  constexpr int NDB = D / 32;           // 32-row blocks of dK^T / dV^T
-  constexpr int NQT = 2 * NDB / kWaves; // dQ 32x32 tiles per wave (2 for d=128, 1 for d=64)
-  constexpr int RB = D * 2;             // bytes per Q / dO / K row
-  __shared__ __attribute__((aligned(16))) BwdSmem<D> sm;
+    const bf16_raw* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dsc,
+    float* __restrict__ dK, float* __restrict__ dV, int N, int n_kvblk, int total, float scale, float c) {
+  constexpr int NKK = D / 16;  // 16-wide head-dim slices (contraction of S and dP)
+  constexpr int NDB = D / 32;  // 32-row blocks of dK^T / dV^T
+  constexpr int RB = D * 2;    // bytes per Q / dO / K row
+  constexpr uint32_t kTileBytes = kBQ * D * 2;
+  constexpr uint32_t kDoutMinusQ = 2 * kTileBytes;  // sm.dout[b] - sm.q[b]
+  constexpr uint32_t kDscMinusL2 = 2 * kBQ * 4;     // sm.dsc[b] - sm.l2[b]
+  __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
 
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
   if (blk >= total) return;
@@ -161,8 +135,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
   const size_t head = (size_t)bh * N * D;
-  const bf16_raw* Kh = K + head;
-  const bf16_raw* Vh = V + head;
 
   const int k0 = kvb * kBKV;
   const int my_key = k0 + 32 * wave + col;
@@ -175,16 +147,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
   const __amdgpu_buffer_rsrc_t lrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(L2 + (size_t)bh * N), (short)0, N * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t drs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(Dvec + (size_t)bh * N), (short)0, N * 4, 0x00020000);
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, head_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, head_bytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Dsc + (size_t)bh * N), (short)0, N * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head), (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head), (short)0, head_bytes, 0x00020000);
 
   QCopy<D> qc;
   qc.init(wave, lane);
-  // Q / dO / L2 / D of one query tile into buffer b
+  // Q / dO / L2 / scale*D of one query tile into buffer b
   // (the tile offset goes into the range-checked per-lane offset, so rows
   // past the end of the head read as zeros)
-  auto issue_qtile = [&](int b, int q0) {
+  auto issue_qtile = [&](uint32_t b, int q0) {
     const uint32_t toff = (uint32_t)q0 * D * 2;
     const uint32_t qb = lds_addr_of(sm.q[b]), gb = lds_addr_of(sm.dout[b]);
 #pragma unroll
@@ -193,13 +167,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
       lds_copy(grs, qc.off[i] + toff, 0u, gb + (uint32_t)(i * kWaves + wave) * 1024u);
     }
     if (wave == 0) lds_copy4(lrs, (uint32_t)(q0 + lane) * 4u, 0u, lds_addr_of(sm.l2[b]));
-    if (wave == 1) lds_copy4(drs, (uint32_t)(q0 + lane) * 4u, 0u, lds_addr_of(sm.dv[b]));
+    if (wave == 1) lds_copy4(drs, (uint32_t)(q0 + lane) * 4u, 0u, lds_addr_of(sm.dsc[b]));
   };
 
   const int q_first = CAUSAL ? k0 : 0;  // k0 is a multiple of kBQ
   const int n_steps = (N - q_first + kBQ - 1) / kBQ;
 
-  // K and V blocks into LDS (natural row order), first query tile
+  // K block into LDS (natural row order), first query tile
   {
     constexpr int KINSTR = kBKV * (D / 8) / kThreads;
     constexpr int SLOTS = D / 8, RPI = 64 / SLOTS;
@@ -209,10 +183,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
       const int slot = lane % SLOTS;
       const uint32_t off = (uint32_t)((k0 + r) * D * 2 + 16 * (slot ^ swz<RB>(r)));
       lds_copy(krs, off, 0u, lds_addr_of(sm.k) + (uint32_t)(i * kWaves + wave) * 1024u);
-      lds_copy(vrs, off, 0u, lds_addr_of(sm.v) + (uint32_t)(i * kWaves + wave) * 1024u);
     }
   }
-  issue_qtile(0, q_first);
+  issue_qtile(0u, q_first);
+
+  // V rows of this wave's keys, 8 head-dim elements per k-slice: the B
+  // operands of dP = dO V^T for the whole kernel (rows past N read as zero)
+  bf16x8 vres[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    vres[kk] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, (uint32_t)(my_key * D + 16 * kk + 8 * g) * 2u, 0, 0));
 
   f32x16 dk_acc[NDB], dv_acc[NDB];
 #pragma unroll
@@ -224,181 +205,162 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
     }
 
   // operand register sets (see pin()): row operands of S / dP, transposed
-  // operands of dV / dK, operands of dQ; P and dS tiles (B operands)
-  bf16x8 ar[2][6], at[2][2], aq[2][3], pb[2][2], dsb[2][2];
+  // operands of dV / dK; P and dS' tiles (B operands)
+  bf16x8 ar[2][5], at[2][2], pb[2][2], dsb[2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int x = 0; x < 6; ++x) ar[j][x] = bf16x8{};
+    for (int x = 0; x < 5; ++x) ar[j][x] = bf16x8{};
 #pragma unroll
     for (int x = 0; x < 2; ++x) at[j][x] = bf16x8{};
-#pragma unroll
-    for (int x = 0; x < 3; ++x) aq[j][x] = bf16x8{};
     pb[j][0] = pb[j][1] = dsb[j][0] = dsb[j][1] = bf16x8{};
   }
 
-  // lane parts of the transpose-read offsets (bytes): rows 4g + (sl >> 2)
-  // of a 16-row group, columns 16 (grp & 1) + 4 (sl & 3) of a 32-wide block
-  const int tr_row = 4 * g + (sl >> 2);     // Q / dO tiles (perm32 row order)
-  const int tk_row = 8 * g + (sl >> 2);     // K and dS^T tiles (natural order)
-  const int tr_col = 16 * (grp & 1) + 4 * (sl & 3);
+  // ---- per-lane LDS address constants.  Every tile base is a multiple of
+  // 1 KiB, so XOR masks below bit 10 pass through the base.
+  // S / dP row reads: row 32 qb + col (Q, dO) or 32 wave + col (K), chunk
+  // 2 kk + g: offset = lane constant ^ (32 kk), + 32 qb rows as an immediate.
+  const int sw_r = swz<RB>(col);
+  const uint32_t row_lane = (uint32_t)(col * RB + 16 * ((g ^ sw_r) & 1) + 32 * (sw_r >> 1));
+  const uint32_t k_row = opaque(lds_addr_of(sm.k) + (uint32_t)(32 * wave * RB) + row_lane);
+  // transpose reads of the Q / dO tiles: rows 16 (2 qb + h) + tr_row (and
+  // + 8), columns 32 db + 8 c0 + 4 (sl & 1) .. + 3
+  const int tr_row = 4 * g + (sl >> 2);
+  const int c0 = 2 * (grp & 1) + ((sl & 3) >> 1);
+  const int sw_t = swz<RB>(tr_row);
+  const uint32_t tq_lane = (uint32_t)(tr_row * RB + 64 * (sw_t >> 2) + 16 * (c0 ^ (sw_t & 3)) + 8 * (sl & 1));
+  const uint32_t q_base0 = lds_addr_of(sm.q[0]);
+  const uint32_t l2_base0 = lds_addr_of(sm.l2[0]);
 
+  wait_loads();
   for (int st = 0; st < n_steps; ++st) {
     const int q0 = q_first + st * kBQ;
-    const int buf = st & 1;
-    wait_loads();
-    __syncthreads();  // tile st visible; every wave is done with step st-1
-    if (st + 1 < n_steps) issue_qtile(buf ^ 1, q0 + kBQ);
-    const char* qt = reinterpret_cast<const char*>(sm.q[buf]);
-    const char* gt = reinterpret_cast<const char*>(sm.dout[buf]);
-    const char* kt = reinterpret_cast<const char*>(sm.k);
-    const char* vt = reinterpret_cast<const char*>(sm.v);
+    const uint32_t buf = (uint32_t)(st & 1);
+    __syncthreads();  // tile st visible; every wave is done with tile st-1
+    if (st + 1 < n_steps) issue_qtile(buf ^ 1u, q0 + kBQ);
+    const uint32_t qbase = q_base0 + buf * kTileBytes;
 
-    // S = Q K^T and dP = dO V^T: 64 query rows (2 blocks) x this wave's 32 keys
+    // ---- A: S = Q K^T and dP = dO V^T, 64 query rows (2 blocks) x this wave's 32 keys
     f32x16 s[2], dp[2];
+    {
+      const uint32_t qrow = opaque(qbase + row_lane);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      bf16x8(&a)[6] = ar[kk & 1];
+      for (int kk = 0; kk < NKK; ++kk) {
+        bf16x8(&a)[5] = ar[kk & 1];
+        const uint32_t ra = qrow ^ (uint32_t)(32 * kk);
+        a[0] = lds_row16(ra);
+        a[1] = lds_row16(ra + 32 * RB);
+        a[2] = lds_row16(ra + kDoutMinusQ);
+        a[3] = lds_row16(ra + kDoutMinusQ + 32 * RB);
+        a[4] = lds_row16(k_row ^ (uint32_t)(32 * kk));
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        a[qb] = as_bf16x8(ld16(qt + slot_off<RB>(32 * qb + col, 2 * kk + g)));
-        a[2 + qb] = as_bf16x8(ld16(gt + slot_off<RB>(32 * qb + col, 2 * kk + g)));
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb] = mfma32(a[qb], a[4], kk == 0 ? f32x16{} : s[qb]);
+          dp[qb] = mfma32(a[2 + qb], vres[kk], kk == 0 ? f32x16{} : dp[qb]);
+          anchor_a(s[qb]);
+          anchor_a(dp[qb]);
+        }
+        group_fence();
+#pragma unroll
+        for (int x = 0; x < 5; ++x) pin(ar[(kk + 1) & 1][x]);
+        if (kk == 0) {  // operands of step st-1's dV / dK products are released
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) pin(at[j][x]);
+          }
+          pin(pb[1][1]);
+          pin(dsb[1][1]);
+        }
       }
-      a[4] = as_bf16x8(ld16(kt + slot_off<RB>(32 * wave + col, 2 * kk + g)));  // K rows of this wave's keys
-      a[5] = as_bf16x8(ld16(vt + slot_off<RB>(32 * wave + col, 2 * kk + g)));
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = mfma32(a[qb], a[4], kk == 0 ? f32x16{} : s[qb]);
-        dp[qb] = mfma32(a[2 + qb], a[5], kk == 0 ? f32x16{} : dp[qb]);
-      }
-      group_fence();
-#pragma unroll
-      for (int x = 0; x < 6; ++x) pin(ar[(kk + 1) & 1][x]);
     }
 
-    // P = exp2(S c - L log2 e) and dS = P (dP - D); masked pairs get 0
+    // ---- B: P = exp2(S c - L log2 e), dS' = P (scale dP - scale D); masked
+    // pairs get 0.  One chunk = 8 query rows (block qb, half h) of each lane.
     const bool need_mask = (CAUSAL && q0 < k0 + kBKV) || k0 + kBKV > N;
-    const float* l2t = sm.l2[buf];
-    const float* dvt = sm.dv[buf];
-    float guard = 0.f;
+    const uint32_t l2_addr = l2_base0 + buf * (kBQ * 4) + (uint32_t)(32 * g);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int qr = 32 * qb + 16 * h + 8 * g;  // 8 consecutive local query rows
-        const float4 l0 = *reinterpret_cast<const float4*>(&l2t[qr]);
-        const float4 l1 = *reinterpret_cast<const float4*>(&l2t[qr + 4]);
-        const float4 d0 = *reinterpret_cast<const float4*>(&dvt[qr]);
-        const float4 d1 = *reinterpret_cast<const float4*>(&dvt[qr + 4]);
-        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-        float p[8], ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float pe = fast_exp2(fmaf(s[qb][8 * h + e], c, -lv[e]));
-          if (need_mask) {
-            const int q = q0 + qr + e;
-            if (my_key >= N || (CAUSAL && my_key > q)) pe = 0.f;
-          }
-          p[e] = pe;
-          ds[e] = pe * (dp[qb][8 * h + e] - dd[e]);
-        }
-        guard += ds[7];
-        pb[qb][h] = pack_bf16x8(p);
-        dsb[qb][h] = pack_bf16x8(ds);
-        // dS^T row = this lane's key, 8 consecutive query rows
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sm.dst) +
-                                  slot_off<kBQ * 2>(32 * wave + col, qr >> 3)) = __builtin_bit_cast(uint4, dsb[qb][h]);
+    for (int ch = 0; ch < 4; ++ch) {
+      const int qb = ch >> 1, h = ch & 1;
+      const uint32_t qr = (uint32_t)(32 * qb + 16 * h);  // + 8 g: 8 consecutive local query rows
+      const f32x4 l0 = *(lds_f4*)(uintptr_t)(l2_addr + 4 * qr);
+      const f32x4 l1 = *(lds_f4*)(uintptr_t)(l2_addr + 4 * qr + 16);
+      const f32x4 d0 = *(lds_f4*)(uintptr_t)(l2_addr + kDscMinusL2 + 4 * qr);
+      const f32x4 d1 = *(lds_f4*)(uintptr_t)(l2_addr + kDscMinusL2 + 4 * qr + 16);
+      const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+      const float dd[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      // masked pairs of this chunk: e < dead (row q0 + qr + 8 g + e sees
+      // key my_key iff my_key <= that row, and only keys below N exist)
+      int dead = 0;
+      if (need_mask) {
+        dead = CAUSAL ? my_key - (q0 + (int)qr + 8 * g) : 0;
+        dead = my_key >= N ? 8 : dead;
       }
-    // S and dP are consumed: all MFMAs issued so far have run
+      float p[8], ds[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int x = 0; x < 6; ++x) pin(ar[j][x], guard);
-#pragma unroll
-      for (int x = 0; x < 2; ++x) pin(at[j][x], guard);
-#pragma unroll
-      for (int x = 0; x < 3; ++x) pin(aq[j][x], guard);
+      for (int e = 0; e < 8; ++e) {
+        float pe = fast_exp2(fmaf(s[qb][8 * h + e], c, -lv[e]));
+        if (need_mask) pe = e < dead ? 0.f : pe;
+        p[e] = pe;
+        ds[e] = pe * fmaf(dp[qb][8 * h + e], scale, -dd[e]);
+      }
+      pb[qb][h] = pack_bf16x8(p);
+      dsb[qb][h] = pack_bf16x8(ds);
     }
 
-    // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 64 query rows;
-    // A operands by transpose reads, one (query block, half) group at a time
+    // ---- C: dV^T += dO^T P and dK^T += Q^T dS', contraction over the 64
+    // query rows; A operands by transpose reads, one (block, half) at a time
+    {
+      const uint32_t tq = opaque(qbase + tq_lane);
+      const uint32_t tq1 = opaque(tq ^ 32u);  // row + 8: swizzle ^ 2
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int gi = (2 * qb + h) * NDB + db;
-          bf16x8(&a)[2] = at[gi & 1];
-          const int r0 = 32 * qb + 16 * h + tr_row;  // rows r0, r0 + 8 hold queries 8g + 0..3, 8g + 4..7
-          const int cc = 32 * db + tr_col;
-          const int o0 = slot_off<RB>(r0, cc >> 3) + 2 * (cc & 7);
-          const int o1 = slot_off<RB>(r0 + 8, cc >> 3) + 2 * (cc & 7);
-          a[0] = tr_pair(gt, o0, o1);
-          a[1] = tr_pair(qt, o0, o1);
-          dv_acc[db] = mfma32(a[0], pb[qb][h], dv_acc[db]);
-          dk_acc[db] = mfma32(a[1], dsb[qb][h], dk_acc[db]);
-          group_fence();
-          pin(at[(gi + 1) & 1][0]);
-          pin(at[(gi + 1) & 1][1]);
-          if (db == 0 && (qb | h)) {  // first group of (qb, h): the previous P / dS pair is released
-            const int pg = 2 * qb + h - 1;
-            pin(pb[pg >> 1][pg & 1]);
-            pin(dsb[pg >> 1][pg & 1]);
+          for (int db = 0; db < NDB; ++db) {
+            const int gi = (2 * qb + h) * NDB + db;
+            bf16x8(&a)[2] = at[gi & 1];
+            const uint32_t rows = (uint32_t)((32 * qb + 16 * h) * RB);
+            const uint32_t o0 = (tq ^ (uint32_t)(64 * db)) + rows;
+            const uint32_t o1 = (tq1 ^ (uint32_t)(64 * db)) + rows + 8 * RB;
+            a[0] = tr_pair(o0 + kDoutMinusQ, o1 + kDoutMinusQ);
+            a[1] = tr_pair(o0, o1);
+            dv_acc[db] = mfma32(a[0], pb[qb][h], dv_acc[db]);
+            dk_acc[db] = mfma32(a[1], dsb[qb][h], dk_acc[db]);
+            anchor_a(dv_acc[db]);
+            anchor_a(dk_acc[db]);
+            group_fence();
+            pin(at[(gi + 1) & 1][0]);
+            pin(at[(gi + 1) & 1][1]);
+            if (gi == 0) {  // operands of the S / dP products are released
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int x = 0; x < 5; ++x) pin(ar[j][x]);
+            }
+            if (db == 0 && (qb | h)) {  // first group of (qb, h): the previous P / dS' pair is released
+              const int pg = 2 * qb + h - 1;
+              pin(pb[pg >> 1][pg & 1]);
+              pin(dsb[pg >> 1][pg & 1]);
+            }
           }
-        }
-    __syncthreads();  // dS^T complete
-
-    // dQ[q][d] += scale sum_key dS[q][key] K[key][d] over the block's keys
-    f32x16 dq[NQT];
-    const char* dtt = reinterpret_cast<const char*>(sm.dst);
-#pragma unroll
-    for (int kk = 0; kk < kBKV / 16; ++kk) {
-      bf16x8(&a)[3] = aq[kk & 1];
-      const int kr0 = 16 * kk + tk_row;  // keys kr0 .. +3 and kr0 + 4 .. +7
-#pragma unroll
-      for (int t = 0; t < NQT; ++t) {
-        const int tt = NQT == 2 ? t : (wave & 1);  // query block of this tile
-        const int cq = 32 * tt + tr_col;
-        a[t] = tr_pair(dtt, slot_off<kBQ * 2>(kr0, cq >> 3) + 2 * (cq & 7),
-                       slot_off<kBQ * 2>(kr0 + 4, cq >> 3) + 2 * (cq & 7));
-      }
-      const int db = NQT == 2 ? wave : (wave >> 1);
-      const int cd = 32 * db + tr_col;
-      a[2] = tr_pair(kt, slot_off<RB>(kr0, cd >> 3) + 2 * (cd & 7), slot_off<RB>(kr0 + 4, cd >> 3) + 2 * (cd & 7));
-#pragma unroll
-      for (int t = 0; t < NQT; ++t) dq[t] = mfma32(a[t], a[2], kk == 0 ? f32x16{} : dq[t]);
-      group_fence();
-#pragma unroll
-      for (int x = 0; x < 3; ++x) pin(aq[(kk + 1) & 1][x]);
     }
-    float qsum = 0.f;
-#pragma unroll
-    for (int t = 0; t < NQT; ++t) {
-      const int tt = NQT == 2 ? t : (wave & 1);
-      const int db = NQT == 2 ? wave : (wave >> 1);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = q0 + 32 * tt + acc_row(i, g);
-        const float v = scale * dq[t][i];
-        qsum += v;
-        if (q < N) unsafeAtomicAdd(dQ + head + (size_t)q * D + 32 * db + col, v);
-      }
-    }
-    // dQ consumed: every MFMA of this step has run
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int x = 0; x < 3; ++x) pin(aq[j][x], qsum);
-#pragma unroll
-      for (int x = 0; x < 2; ++x) pin(at[j][x], qsum);
-      pin(pb[j][0], qsum);
-      pin(pb[j][1], qsum);
-      pin(dsb[j][0], qsum);
-      pin(dsb[j][1], qsum);
-    }
+    wait_loads();  // this wave's copies of tile st+1 have landed
   }
+
+  // every MFMA has completed once fin exists: operand registers may be reused
+  const float fin = dk_acc[NDB - 1][0] + dv_acc[NDB - 1][0];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) pin(at[j][x], fin);
+    pin(pb[j][0], fin);
+    pin(pb[j][1], fin);
+    pin(dsb[j][0], fin);
+    pin(dsb[j][1], fin);
+  }
+  group_fence();  // nothing after this point is scheduled above the pins
 
   if (my_key < N) {
     float* dKrow = dK + head + (size_t)my_key * D;
@@ -409,8 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = 32 * db + 8 * i4 + 4 * g;
         *reinterpret_cast<float4*>(dKrow + d) =
-            make_float4(scale * dk_acc[db][4 * i4], scale * dk_acc[db][4 * i4 + 1], scale * dk_acc[db][4 * i4 + 2],
-                        scale * dk_acc[db][4 * i4 + 3]);
+            make_float4(dk_acc[db][4 * i4], dk_acc[db][4 * i4 + 1], dk_acc[db][4 * i4 + 2], dk_acc[db][4 * i4 + 3]);
         *reinterpret_cast<float4*>(dVrow + d) =
             make_float4(dv_acc[db][4 * i4], dv_acc[db][4 * i4 + 1], dv_acc[db][4 * i4 + 2], dv_acc[db][4 * i4 + 3]);
       }
@@ -426,18 +387,20 @@ hipError_t launch(const void* q, const void* k, const void* v, const float* o, c
   const int n_kvblk = (N + kBKV - 1) / kBKV;
   const long long total = (long long)BH * n_kvblk;
   if (pre_grid > (1LL << 31) - 1 || total > (1LL << 30)) return hipErrorInvalidConfiguration;
-  float* dvec = ws;
+  float* dsc = ws;
   float* l2 = ws + rows;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_grid), dim3(256), 0, stream,
-                     static_cast<const bf16_raw*>(dout), o, lse, dvec, l2, dq, rows);
+                     static_cast<const bf16_raw*>(dout), o, lse, dsc, l2, rows, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = (int)((total + 7) / 8 * 8);
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k), static_cast<const bf16_raw*>(v),
-                     static_cast<const bf16_raw*>(dout), l2, dvec, dq, dk, dv, N, n_kvblk, (int)total, scale,
+                     static_cast<const bf16_raw*>(dout), l2, dsc, dk, dv, N, n_kvblk, (int)total, scale,
                      scale * kLog2e);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq_bf16(q, k, v, dout, l2, dsc, dq, BH, N, D, scale, CAUSAL ? 1 : 0, stream);
 }
 
 }  // namespace

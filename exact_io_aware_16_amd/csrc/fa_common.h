@@ -52,12 +52,21 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // in the meantime; the compiler does not guard that write-after-read.  The
 // kernels therefore rotate operand registers through two sets and release a
 // set only after the next group of MFMAs has been issued:
+//   anchor_*(acc)  -- empty asm that takes (and formally rewrites) an MFMA
+//                     result: the product is a pure value, so without it the
+//                     instruction selector may place the MFMA after the fence
+//                     that follows; with it the MFMA is emitted before the
+//                     anchor.  anchor_v for results kept in VGPRs, anchor_a
+//                     for results kept in AGPRs (the wrong class costs copies);
 //   group_fence()  -- no instruction is scheduled across it, so every MFMA of
-//                     the group before it is issued before anything after it;
+//                     the group before it (anchored) is issued before
+//                     anything after it;
 //   pin(v)         -- empty asm reading v: keeps v's registers live (and not
 //                     reused) up to this point.  Emits no code.
 // At the end of a phase, pin(v, x) with x computed from all of the phase's
 // MFMA results keeps the operands live until those MFMAs have completed.
+__device__ __forceinline__ void anchor_v(f32x16& acc) { asm volatile("" : "+v"(acc)); }
+__device__ __forceinline__ void anchor_a(f32x16& acc) { asm volatile("" : "+a"(acc)); }
 __device__ __forceinline__ void group_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ __forceinline__ void pin(const bf16x8& v) { asm volatile("" ::"v"(v)); }
 __device__ __forceinline__ void pin(const bf16x8& v, float after) { asm volatile("" ::"v"(v), "v"(after)); }

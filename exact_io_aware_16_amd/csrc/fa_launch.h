@@ -13,6 +13,12 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N,
                           int d, float scale, int causal, hipStream_t stream);
 
+// dQ only, query-stationary (fa_bwd_dq.hip); l2 and dsc are the per-row
+// L log2(e) and scale * D written by the backward preprocess.
+hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
+                              const float* dsc, float* dq, int BH, int N, int d, float scale, int causal,
+                              hipStream_t stream);
+
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* dvec, int BH, int N,
                            int d, float scale, int causal, hipStream_t stream);

@@ -48,7 +48,9 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL                          */
-  FA_ERR_SHAPE = 2,     /* B, H or N negative, causal not 0/1, or size overflow */
+  FA_ERR_SHAPE = 2,     /* B, H or N negative, causal not 0/1, B*H above
+                           INT32_MAX, or N*d*4 above INT32_MAX (one head of a
+                           float32 tensor must be byte-addressable in 31 bits) */
   FA_ERR_HEADDIM = 3,   /* d is not a supported head width (64 or 128)         */
   FA_ERR_SCALE = 4,     /* scale is not finite and > 0                         */
   FA_ERR_WORKSPACE = 5, /* backward workspace missing                          */
@@ -79,8 +81,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 /*
  * Bytes of device workspace fa_bwd needs: two float32 per query row
- * (D_i = dO_i . O_i and L_i log2(e)).  Returns 0 for an empty or invalid
- * shape.
+ * (scale * D_i with D_i = dO_i . O_i, and L_i log2(e)).  Returns 0 for an
+ * empty or invalid shape.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -93,8 +95,11 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   workspace     : device, >= fa_bwd_workspace_bytes(B,H,N,d) bytes; its
  *                   contents on entry do not matter
  * The probability tiles are rebuilt from Q, K and lse; no N x N tensor is
- * stored.  dq is accumulated with float32 atomics, so its low bits may vary
- * from run to run; dk and dv are deterministic.
+ * stored.  Three kernels run on `stream`: a per-row preprocess, a
+ * key-stationary pass for dk and dv, and a query-stationary pass for dq
+ * (which recomputes the score tiles instead of summing partial dq with
+ * atomics).  Every output element is written once: results are
+ * deterministic.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
            const void* dout, float* dq, float* dk, float* dv, void* workspace,
