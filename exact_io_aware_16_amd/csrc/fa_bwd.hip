@@ -88,7 +88,6 @@ constexpr int kBQ = 64;            // query rows per step
 
 template <int D>
 struct DkdvSmem {
-  bf16_raw k[kBKV * D];          // K block, rows in key order
   bf16_raw q[2][kBQ * D];        // Q tiles, rows in perm32 order
   bf16_raw dout[2][kBQ * D];     // dO tiles, rows in perm32 order
   float l2[2][kBQ];              // L log2(e) of the tile's rows
@@ -173,27 +172,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int q_first = CAUSAL ? k0 : 0;  // k0 is a multiple of kBQ
   const int n_steps = (N - q_first + kBQ - 1) / kBQ;
 
-  // K block into LDS (natural row order), first query tile
-  {
-    constexpr int KINSTR = kBKV * (D / 8) / kThreads;
-    constexpr int SLOTS = D / 8, RPI = 64 / SLOTS;
-#pragma unroll
-    for (int i = 0; i < KINSTR; ++i) {
-      const int r = (i * kWaves + wave) * RPI + lane / SLOTS;
-      const int slot = lane % SLOTS;
-      const uint32_t off = (uint32_t)((k0 + r) * D * 2 + 16 * (slot ^ swz<RB>(r)));
-      lds_copy(krs, off, 0u, lds_addr_of(sm.k) + (uint32_t)(i * kWaves + wave) * 1024u);
-    }
-  }
   issue_qtile(0u, q_first);
 
-  // V rows of this wave's keys, 8 head-dim elements per k-slice: the B
-  // operands of dP = dO V^T for the whole kernel (rows past N read as zero)
-  bf16x8 vres[NKK];
+  // K and V rows of this wave's keys, 8 head-dim elements per k-slice: the
+  // B operands of S = Q K^T and dP = dO V^T for the whole kernel (rows past
+  // N read as zero)
+  bf16x8 kres[NKK], vres[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-    vres[kk] = __builtin_bit_cast(
-        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, (uint32_t)(my_key * D + 16 * kk + 8 * g) * 2u, 0, 0));
+  for (int kk = 0; kk < NKK; ++kk) {
+    const uint32_t off = (uint32_t)(my_key * D + 16 * kk + 8 * g) * 2u;
+    kres[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+    vres[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+    // kept in AGPRs, which the matrix cores read directly
+    asm volatile("" : "+a"(kres[kk]));
+    asm volatile("" : "+a"(vres[kk]));
+  }
 
   f32x16 dk_acc[NDB], dv_acc[NDB];
 #pragma unroll
@@ -204,25 +197,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       dv_acc[db][i] = 0.f;
     }
 
-  // operand register sets (see pin()): row operands of S / dP, transposed
-  // operands of dV / dK; P and dS' tiles (B operands)
-  bf16x8 ar[2][5], at[2][2], pb[2][2], dsb[2][2];
+  // Operand register sets (see pin()).  Each MFMA phase keeps three sets and
+  // loads group g + 2 while group g runs: the set it overwrites was last
+  // read by group g - 1, which has started once group g is issued.
+  //   ar: Q / dO rows of the S and dP products (one query block, k-slice)
+  //   at: dO^T / Q^T transpose reads of the dV and dK products
+  //   pb, dsb: P and dS' tiles (B operands)
+  constexpr int NCG = 4 * NDB;  // (query block, half, head-dim block) groups of phase C
+  constexpr int NAG = 2 * NKK;   // (k-slice, query block) groups of phase A
+  bf16x8 ar[3][2], at[3][2], pb[2][2], dsb[2][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 3; ++j) ar[j][0] = ar[j][1] = at[j][0] = at[j][1] = bf16x8{};
 #pragma unroll
-    for (int x = 0; x < 5; ++x) ar[j][x] = bf16x8{};
-#pragma unroll
-    for (int x = 0; x < 2; ++x) at[j][x] = bf16x8{};
-    pb[j][0] = pb[j][1] = dsb[j][0] = dsb[j][1] = bf16x8{};
-  }
+  for (int j = 0; j < 2; ++j) pb[j][0] = pb[j][1] = dsb[j][0] = dsb[j][1] = bf16x8{};
 
   // ---- per-lane LDS address constants.  Every tile base is a multiple of
   // 1 KiB, so XOR masks below bit 10 pass through the base.
-  // S / dP row reads: row 32 qb + col (Q, dO) or 32 wave + col (K), chunk
-  // 2 kk + g: offset = lane constant ^ (32 kk), + 32 qb rows as an immediate.
+  // S / dP row reads: row 32 qb + col, chunk 2 kk + g:
+  // offset = lane constant ^ (32 kk), + 32 qb rows as an immediate.
   const int sw_r = swz<RB>(col);
   const uint32_t row_lane = (uint32_t)(col * RB + 16 * ((g ^ sw_r) & 1) + 32 * (sw_r >> 1));
-  const uint32_t k_row = opaque(lds_addr_of(sm.k) + (uint32_t)(32 * wave * RB) + row_lane);
   // transpose reads of the Q / dO tiles: rows 16 (2 qb + h) + tr_row (and
   // + 8), columns 32 db + 8 c0 + 4 (sl & 1) .. + 3
   const int tr_row = 4 * g + (sl >> 2);
@@ -240,111 +234,134 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     if (st + 1 < n_steps) issue_qtile(buf ^ 1u, q0 + kBQ);
     const uint32_t qbase = q_base0 + buf * kTileBytes;
 
-    // ---- A: S = Q K^T and dP = dO V^T, 64 query rows (2 blocks) x this wave's 32 keys
+    // The step runs as four MFMA phases; the softmax of one query block
+    // runs on the vector ALUs between the MFMA groups of the next phase:
+    //   A0: S, dP of query block 0      A1: S, dP of block 1  + softmax(0)
+    //   C0: dV, dK from block 0 + softmax(1)      C1: dV, dK from block 1
     f32x16 s[2], dp[2];
-    {
-      const uint32_t qrow = opaque(qbase + row_lane);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        bf16x8(&a)[5] = ar[kk & 1];
-        const uint32_t ra = qrow ^ (uint32_t)(32 * kk);
-        a[0] = lds_row16(ra);
-        a[1] = lds_row16(ra + 32 * RB);
-        a[2] = lds_row16(ra + kDoutMinusQ);
-        a[3] = lds_row16(ra + kDoutMinusQ + 32 * RB);
-        a[4] = lds_row16(k_row ^ (uint32_t)(32 * kk));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[qb] = mfma32(a[qb], a[4], kk == 0 ? f32x16{} : s[qb]);
-          dp[qb] = mfma32(a[2 + qb], vres[kk], kk == 0 ? f32x16{} : dp[qb]);
-          anchor_a(s[qb]);
-          anchor_a(dp[qb]);
-        }
-        group_fence();
-#pragma unroll
-        for (int x = 0; x < 5; ++x) pin(ar[(kk + 1) & 1][x]);
-        if (kk == 0) {  // operands of step st-1's dV / dK products are released
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-#pragma unroll
-            for (int x = 0; x < 2; ++x) pin(at[j][x]);
-          }
-          pin(pb[1][1]);
-          pin(dsb[1][1]);
-        }
-      }
-    }
+    const uint32_t qrow = opaque(qbase + row_lane);
+    // phase-A group ga = NKK qb + kk: Q and dO rows of block qb, k-slice kk
+    auto load_a = [&](int ga) {
+      const int qb = ga / NKK, kk = ga % NKK;
+      const uint32_t ra = (qrow ^ (uint32_t)(32 * kk)) + (uint32_t)(32 * qb * RB);
+      ar[ga % 3][0] = lds_row16(ra);
+      ar[ga % 3][1] = lds_row16(ra + kDoutMinusQ);
+    };
+    const uint32_t tq = opaque(qbase + tq_lane);
+    const uint32_t tq1 = opaque(tq ^ 32u);  // row + 8: swizzle ^ 2
+    // phase-C group gi = NDB (2 qb + h) + db
+    auto load_c = [&](int gi) {
+      const int qh = gi / NDB, db = gi % NDB;  // qh = 2 qb + h
+      bf16x8(&a)[2] = at[gi % 3];
+      const uint32_t rows = (uint32_t)(16 * qh * RB);
+      const uint32_t o0 = (tq ^ (uint32_t)(64 * db)) + rows;
+      const uint32_t o1 = (tq1 ^ (uint32_t)(64 * db)) + rows + 8 * RB;
+      a[0] = tr_pair(o0 + kDoutMinusQ, o1 + kDoutMinusQ);
+      a[1] = tr_pair(o0, o1);
+    };
 
-    // ---- B: P = exp2(S c - L log2 e), dS' = P (scale dP - scale D); masked
-    // pairs get 0.  One chunk = 8 query rows (block qb, half h) of each lane.
+    // ---- softmax of query block qb in 8 pieces of 2 elements per lane:
+    // P = exp2(S c - L log2 e), dS' = P (scale dP - scale D); masked pairs get 0
     const bool need_mask = (CAUSAL && q0 < k0 + kBKV) || k0 + kBKV > N;
     const uint32_t l2_addr = l2_base0 + buf * (kBQ * 4) + (uint32_t)(32 * g);
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const int qb = ch >> 1, h = ch & 1;
+    float lv[8], dd[8], pv[8], dv8[8];
+    int dead = 0;
+    auto softmax_piece = [&](int qb, int piece) {
+      const int h = piece >> 2, e0 = 2 * (piece & 3);
       const uint32_t qr = (uint32_t)(32 * qb + 16 * h);  // + 8 g: 8 consecutive local query rows
-      const f32x4 l0 = *(lds_f4*)(uintptr_t)(l2_addr + 4 * qr);
-      const f32x4 l1 = *(lds_f4*)(uintptr_t)(l2_addr + 4 * qr + 16);
-      const f32x4 d0 = *(lds_f4*)(uintptr_t)(l2_addr + kDscMinusL2 + 4 * qr);
-      const f32x4 d1 = *(lds_f4*)(uintptr_t)(l2_addr + kDscMinusL2 + 4 * qr + 16);
-      const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-      const float dd[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-      // masked pairs of this chunk: e < dead (row q0 + qr + 8 g + e sees
-      // key my_key iff my_key <= that row, and only keys below N exist)
-      int dead = 0;
-      if (need_mask) {
-        dead = CAUSAL ? my_key - (q0 + (int)qr + 8 * g) : 0;
-        dead = my_key >= N ? 8 : dead;
-      }
-      float p[8], ds[8];
+      if ((piece & 3) == 0) {
+        const f32x4 l0 = *(lds_f4*)(uintptr_t)(l2_addr + 4 * qr);
+        const f32x4 l1 = *(lds_f4*)(uintptr_t)(l2_addr + 4 * qr + 16);
+        const f32x4 d0 = *(lds_f4*)(uintptr_t)(l2_addr + kDscMinusL2 + 4 * qr);
+        const f32x4 d1 = *(lds_f4*)(uintptr_t)(l2_addr + kDscMinusL2 + 4 * qr + 16);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
+          lv[e] = l0[e];
+          lv[4 + e] = l1[e];
+          dd[e] = d0[e];
+          dd[4 + e] = d1[e];
+        }
+        // masked pairs of this chunk: e < dead (row q0 + qr + 8 g + e sees
+        // key my_key iff my_key <= that row, and only keys below N exist)
+        if (need_mask) {
+          dead = CAUSAL ? my_key - (q0 + (int)qr + 8 * g) : 0;
+          dead = my_key >= N ? 8 : dead;
+        }
+      }
+#pragma unroll
+      for (int e = e0; e < e0 + 2; ++e) {
         float pe = fast_exp2(fmaf(s[qb][8 * h + e], c, -lv[e]));
         if (need_mask) pe = e < dead ? 0.f : pe;
-        p[e] = pe;
-        ds[e] = pe * fmaf(dp[qb][8 * h + e], scale, -dd[e]);
+        pv[e] = pe;
+        dv8[e] = pe * fmaf(dp[qb][8 * h + e], scale, -dd[e]);
       }
-      pb[qb][h] = pack_bf16x8(p);
-      dsb[qb][h] = pack_bf16x8(ds);
+      if ((piece & 3) == 3) {
+        pb[qb][h] = pack_bf16x8(pv);
+        dsb[qb][h] = pack_bf16x8(dv8);
+      }
+    };
+
+    // ---- A0, A1: S = Q K^T and dP = dO V^T, 32 query rows x this wave's 32 keys each
+    load_a(0);
+    load_a(1);
+#pragma unroll
+    for (int ga = 0; ga < NAG; ++ga) {
+      const int qb = ga / NKK, kk = ga % NKK;
+      s[qb] = mfma32(ar[ga % 3][0], kres[kk], kk == 0 ? f32x16{} : s[qb]);
+      dp[qb] = mfma32(ar[ga % 3][1], vres[kk], kk == 0 ? f32x16{} : dp[qb]);
+      anchor_a(s[qb]);
+      anchor_a(dp[qb]);
+      group_fence();
+      if (ga == 0) {  // operands of step st-1's dV / dK products are released
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          pin(at[j][0]);
+          pin(at[j][1]);
+        }
+        pin(pb[1][1]);
+        pin(dsb[1][1]);
+      }
+      pin(ar[(ga + 2) % 3][0]);
+      pin(ar[(ga + 2) % 3][1]);
+      if (ga + 2 < NAG) load_a(ga + 2);
+      if (ga + 2 == NAG) load_c(0);
+      if (ga + 1 == NAG) load_c(1);
+      if (qb == 1) {  // softmax of block 0 while block 1's products run
+#pragma unroll
+        for (int pc = 0; pc < 8 / NKK; ++pc) softmax_piece(0, kk * (8 / NKK) + pc);
+      }
     }
 
-    // ---- C: dV^T += dO^T P and dK^T += Q^T dS', contraction over the 64
-    // query rows; A operands by transpose reads, one (block, half) at a time
-    {
-      const uint32_t tq = opaque(qbase + tq_lane);
-      const uint32_t tq1 = opaque(tq ^ 32u);  // row + 8: swizzle ^ 2
+    // ---- C0, C1: dV^T += dO^T P and dK^T += Q^T dS', contraction over the
+    // query rows; A operands by transpose reads
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+    for (int gi = 0; gi < NCG; ++gi) {
+      const int qh = gi / NDB, db = gi % NDB;
+      const int qb = qh >> 1, h = qh & 1;
+      bf16x8(&a)[2] = at[gi % 3];
+      dv_acc[db] = mfma32(a[0], pb[qb][h], dv_acc[db]);
+      dk_acc[db] = mfma32(a[1], dsb[qb][h], dk_acc[db]);
+      anchor_a(dv_acc[db]);
+      anchor_a(dk_acc[db]);
+      group_fence();
+      if (gi == 0) {  // operands of the S / dP products are released
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int j = 0; j < 3; ++j) {
+          pin(ar[j][0]);
+          pin(ar[j][1]);
+        }
+      }
+      if (db == 0 && qh > 0) {  // first group of (qb, h): the previous P / dS' pair is released
+        pin(pb[(qh - 1) >> 1][(qh - 1) & 1]);
+        pin(dsb[(qh - 1) >> 1][(qh - 1) & 1]);
+      }
+      pin(at[(gi + 2) % 3][0]);
+      pin(at[(gi + 2) % 3][1]);
+      if (gi + 2 < NCG) load_c(gi + 2);
+      if (qb == 0) {  // softmax of block 1 while block 0's products run
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int gi = (2 * qb + h) * NDB + db;
-            bf16x8(&a)[2] = at[gi & 1];
-            const uint32_t rows = (uint32_t)((32 * qb + 16 * h) * RB);
-            const uint32_t o0 = (tq ^ (uint32_t)(64 * db)) + rows;
-            const uint32_t o1 = (tq1 ^ (uint32_t)(64 * db)) + rows + 8 * RB;
-            a[0] = tr_pair(o0 + kDoutMinusQ, o1 + kDoutMinusQ);
-            a[1] = tr_pair(o0, o1);
-            dv_acc[db] = mfma32(a[0], pb[qb][h], dv_acc[db]);
-            dk_acc[db] = mfma32(a[1], dsb[qb][h], dk_acc[db]);
-            anchor_a(dv_acc[db]);
-            anchor_a(dk_acc[db]);
-            group_fence();
-            pin(at[(gi + 1) & 1][0]);
-            pin(at[(gi + 1) & 1][1]);
-            if (gi == 0) {  // operands of the S / dP products are released
-#pragma unroll
-              for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int x = 0; x < 5; ++x) pin(ar[j][x]);
-            }
-            if (db == 0 && (qb | h)) {  // first group of (qb, h): the previous P / dS' pair is released
-              const int pg = 2 * qb + h - 1;
-              pin(pb[pg >> 1][pg & 1]);
-              pin(dsb[pg >> 1][pg & 1]);
-            }
-          }
+        for (int pc = 0; pc < 4 / NDB; ++pc) softmax_piece(1, gi * (4 / NDB) + pc);
+      }
     }
     wait_loads();  // this wave's copies of tile st+1 have landed
   }
@@ -352,9 +369,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // every MFMA has completed once fin exists: operand registers may be reused
   const float fin = dk_acc[NDB - 1][0] + dv_acc[NDB - 1][0];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 3; ++j) {
+    pin(at[j][0], fin);
+    pin(at[j][1], fin);
+  }
 #pragma unroll
-    for (int x = 0; x < 2; ++x) pin(at[j][x], fin);
+  for (int j = 0; j < 2; ++j) {
     pin(pb[j][0], fin);
     pin(pb[j][1], fin);
     pin(dsb[j][0], fin);

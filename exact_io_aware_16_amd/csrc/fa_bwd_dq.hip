@@ -134,16 +134,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq_acc[db][i] = 0.f;
 
-  // operand register sets (see pin()): K / V rows of the score products,
-  // K^T operands of the dQ product; dS' tiles (B operands)
-  bf16x8 ar[2][2 * NKB], at[2][NDB], dsb[NKB][2];
+  // Operand register sets (see pin()).  Each MFMA phase keeps three sets
+  // and loads group g + 2 while group g runs: the set it overwrites was last
+  // read by group g - 1, which has started once group g is issued.
+  //   ar: K and V rows of the S^T and dP^T products (one key block, k-slice)
+  //   at: K^T transpose reads of the dQ product (two head-dim blocks)
+  //   dsb: dS'^T tiles (B operands)
+  constexpr int NAG = NKB * NKK;      // (key block, k-slice) groups of the score phase
+  constexpr int NDG = NKB * NDB;      // (key block, half, pair of head-dim blocks) groups of the dQ phase
+  constexpr int PPA = 8 / NKK;        // softmax pieces per score group
+  constexpr int PPD = 8 / (2 * (NDB / 2));  // softmax pieces per dQ group of key block 0
+  bf16x8 ar[3][2], at[3][2], dsb[NKB][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int x = 0; x < 2 * NKB; ++x) ar[j][x] = bf16x8{};
-#pragma unroll
-    for (int x = 0; x < NDB; ++x) at[j][x] = bf16x8{};
-  }
+  for (int j = 0; j < 3; ++j) ar[j][0] = ar[j][1] = at[j][0] = at[j][1] = bf16x8{};
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) dsb[kb][0] = dsb[kb][1] = bf16x8{};
 
@@ -158,6 +161,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int sw_t = swz<RB>(tr_row);
   const uint32_t tk_lane = (uint32_t)(tr_row * RB + 64 * (sw_t >> 2) + 16 * (c0 ^ (sw_t & 3)) + 8 * (sl & 1));
   const uint32_t k_base0 = lds_addr_of(sm.k[0]);
+  const int last_key = CAUSAL ? min(my_q, N - 1) : N - 1;  // keys above are masked
 
   for (int t = 0; t < n_tiles; ++t) {
     const int key0 = t * BC;
@@ -169,90 +173,104 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     if (t + 1 < n_tiles) issue_tile(buf ^ 1u, key0 + BC);
     const uint32_t kbase = k_base0 + buf * kTileBytes;
 
-    // S^T = K Q^T and dP^T = V dO^T: BC keys x this wave's 32 queries
+    // The tile runs as MFMA phases per 32-key block; the softmax of one
+    // block runs on the vector ALUs between the MFMA groups of the next:
+    //   S^T, dP^T of block 0 | of block 1 + softmax(0) | ... |
+    //   dQ from block 0 + softmax(last) | dQ from the other blocks
     f32x16 st[NKB], dpt[NKB];
-    {
-      const uint32_t krow = opaque(kbase + row_lane);
+    const uint32_t krow = opaque(kbase + row_lane);
+    auto load_a = [&](int ga) {
+      const int kb = ga / NKK, kk = ga % NKK;
+      const uint32_t ra = (krow ^ (uint32_t)(32 * kk)) + (uint32_t)(32 * kb * RB);
+      ar[ga % 3][0] = lds_row16(ra);
+      ar[ga % 3][1] = lds_row16(ra + kVMinusK);
+    };
+    const uint32_t tk = opaque(kbase + tk_lane);
+    const uint32_t tk1 = opaque(tk ^ 32u);  // row + 8: swizzle ^ 2
+    // dQ group gd = (2 kb + h) (NDB / 2) + pair: head-dim blocks 2 pair, 2 pair + 1
+    auto load_d = [&](int gd) {
+      const int kh = gd / (NDB / 2), pr = gd % (NDB / 2);
+      const uint32_t rows = (uint32_t)(16 * kh * RB);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        bf16x8(&a)[2 * NKB] = ar[kk & 1];
-        const uint32_t ra = krow ^ (uint32_t)(32 * kk);
+      for (int x = 0; x < 2; ++x) {
+        const int db = 2 * pr + x;
+        at[gd % 3][x] = tr_pair((tk ^ (uint32_t)(64 * db)) + rows, (tk1 ^ (uint32_t)(64 * db)) + rows + 8 * RB);
+      }
+    };
+
+    // dS'^T = P^T (scale dP^T - scale D), P^T = exp2(S^T c - L log2 e), in
+    // 8 pieces of 2 elements per lane; masked pairs get 0
+    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > N;
+    float dsv[8];
+    auto softmax_piece = [&](int kb, int piece) {
+      const int h = piece >> 2, e0 = 2 * (piece & 3);
+      // register 8 h + e of half g holds key key0 + 32 kb + 16 h + 8 g + e
+      const int lim = last_key - (key0 + 32 * kb + 16 * h + 8 * g);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          a[kb] = lds_row16(ra + (uint32_t)(32 * kb * RB));
-          a[NKB + kb] = lds_row16(ra + kVMinusK + (uint32_t)(32 * kb * RB));
+      for (int e = e0; e < e0 + 2; ++e) {
+        float pe = fast_exp2(fmaf(st[kb][8 * h + e], c, -l2q));
+        if (need_mask) pe = e > lim ? 0.f : pe;
+        dsv[e] = pe * fmaf(dpt[kb][8 * h + e], scale, -dq_sc);
+      }
+      if ((piece & 3) == 3) dsb[kb][h] = pack_bf16x8(dsv);
+    };
+
+    // ---- S^T = K Q^T and dP^T = V dO^T, one 32-key block per phase
+    load_a(0);
+    load_a(1);
+#pragma unroll
+    for (int ga = 0; ga < NAG; ++ga) {
+      const int kb = ga / NKK, kk = ga % NKK;
+      st[kb] = mfma32(ar[ga % 3][0], qf[kk], kk == 0 ? f32x16{} : st[kb]);
+      dpt[kb] = mfma32(ar[ga % 3][1], dof[kk], kk == 0 ? f32x16{} : dpt[kb]);
+      anchor_a(st[kb]);
+      anchor_a(dpt[kb]);
+      group_fence();
+      if (ga == 0) {  // operands of tile t-1's dQ product are released
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          pin(at[j][0]);
+          pin(at[j][1]);
         }
+        pin(dsb[NKB - 1][1]);
+      }
+      pin(ar[(ga + 2) % 3][0]);
+      pin(ar[(ga + 2) % 3][1]);
+      if (ga + 2 < NAG) load_a(ga + 2);
+      if (ga + 2 == NAG) load_d(0);
+      if (ga + 1 == NAG) load_d(1);
+      if (kb > 0) {  // softmax of the previous block
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          st[kb] = mfma32(a[kb], qf[kk], kk == 0 ? f32x16{} : st[kb]);
-          dpt[kb] = mfma32(a[NKB + kb], dof[kk], kk == 0 ? f32x16{} : dpt[kb]);
-          anchor_a(st[kb]);
-          anchor_a(dpt[kb]);
-        }
-        group_fence();
-#pragma unroll
-        for (int x = 0; x < 2 * NKB; ++x) pin(ar[(kk + 1) & 1][x]);
-        if (kk == 0) {  // operands of tile t-1's dQ product are released
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int x = 0; x < NDB; ++x) pin(at[j][x]);
-          pin(dsb[NKB - 1][1]);
-        }
+        for (int pc = 0; pc < PPA; ++pc) softmax_piece(kb - 1, kk * PPA + pc);
       }
     }
 
-    // dS'^T = P^T (scale dP^T - scale D), P^T = exp2(S^T c - L log2 e); masked pairs get 0
-    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > N;
-    const int last_key = CAUSAL ? min(my_q, N - 1) : N - 1;  // keys above are masked
+    // ---- dQ^T += K^T dS'^T, K^T by transpose reads of the K tile
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int gd = 0; gd < NDG; ++gd) {
+      const int kh = gd / (NDB / 2), pr = gd % (NDB / 2);
+      const int kb = kh >> 1, h = kh & 1;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // register 8 h + e of half g holds key key0 + 32 kb + 16 h + 8 g + e
-        const int lim = last_key - (key0 + 32 * kb + 16 * h + 8 * g);
-        float ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float pe = fast_exp2(fmaf(st[kb][8 * h + e], c, -l2q));
-          if (need_mask) pe = e > lim ? 0.f : pe;
-          ds[e] = pe * fmaf(dpt[kb][8 * h + e], scale, -dq_sc);
-        }
-        dsb[kb][h] = pack_bf16x8(ds);
+      for (int x = 0; x < 2; ++x) {
+        dq_acc[2 * pr + x] = mfma32(at[gd % 3][x], dsb[kb][h], dq_acc[2 * pr + x]);
+        anchor_a(dq_acc[2 * pr + x]);
       }
-
-    // dQ^T += K^T dS'^T, K^T by transpose reads of the K tile; operand sets
-    // rotate per (key block, half) group
-    {
-      const uint32_t tk = opaque(kbase + tk_lane);
-      const uint32_t tk1 = opaque(tk ^ 32u);  // row + 8: swizzle ^ 2
+      group_fence();
+      if (gd == 0) {  // operands of the score products are released
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int gi = 2 * kb + h;
-          bf16x8(&a)[NDB] = at[gi & 1];
-          const uint32_t rows = (uint32_t)((32 * kb + 16 * h) * RB);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            a[db] = tr_pair((tk ^ (uint32_t)(64 * db)) + rows, (tk1 ^ (uint32_t)(64 * db)) + rows + 8 * RB);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dq_acc[db] = mfma32(a[db], dsb[kb][h], dq_acc[db]);
-            anchor_a(dq_acc[db]);
-          }
-          group_fence();
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) pin(at[(gi + 1) & 1][db]);
-          if (gi == 0) {  // operands of the score products are released
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-              for (int x = 0; x < 2 * NKB; ++x) pin(ar[j][x]);
-          } else {  // the previous dS' group is released
-            pin(dsb[(gi - 1) >> 1][(gi - 1) & 1]);
-          }
+        for (int j = 0; j < 3; ++j) {
+          pin(ar[j][0]);
+          pin(ar[j][1]);
         }
+      }
+      if (pr == 0 && kh > 0) pin(dsb[(kh - 1) >> 1][(kh - 1) & 1]);  // the previous dS' group is released
+      pin(at[(gd + 2) % 3][0]);
+      pin(at[(gd + 2) % 3][1]);
+      if (gd + 2 < NDG) load_d(gd + 2);
+      if (kb == 0) {  // softmax of the last block
+#pragma unroll
+        for (int pc = 0; pc < PPD; ++pc) softmax_piece(NKB - 1, gd * PPD + pc);
+      }
     }
   }
 
@@ -261,9 +279,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 #pragma unroll
   for (int db = 0; db < NDB; ++db) fin += dq_acc[db][0];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int x = 0; x < NDB; ++x) pin(at[j][x], fin);
+  for (int j = 0; j < 3; ++j) {
+    pin(at[j][0], fin);
+    pin(at[j][1], fin);
+  }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     pin(dsb[kb][0], fin);
