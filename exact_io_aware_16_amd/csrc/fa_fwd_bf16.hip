@@ -32,8 +32,10 @@
 //  * P is rounded to bf16 in registers and used directly as the B operand
 //    (the perm32 key order makes the S result layout equal to the operand
 //    layout);
-//  * software pipelined: while the softmax of tile t runs on the vector ALU,
-//    the matrix cores already compute S for tile t+1;
+//  * two waves per SIMD hide each other's softmax behind matrix-core work:
+//    two 4-wave workgroups per CU when the grid is large enough, otherwise
+//    one 8-wave workgroup whose two halves take half of the key tiles each
+//    (split-KV inside the workgroup, merged through LDS at the end);
 //  * causal: query block qb visits key tiles up to its diagonal only, masks
 //    are applied only on tiles that straddle the diagonal or the ragged end.
 #include "fa_common.h"
@@ -45,6 +47,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;        // query rows per workgroup
+constexpr int kComputeUnits = 256;      // MI355X
 constexpr float kRescaleSlack = 8.0f;   // log2 units: P <= 256 before a forced rescale
 
 template <int D> struct FwdTile;
@@ -55,11 +58,12 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <int D>
+// SPLIT key ranges per workgroup, each with its own double-buffered tiles
+template <int D, int SPLIT>
 struct FwdSmem {
   static constexpr int BC = FwdTile<D>::BC;
-  bf16_raw k[2][BC * D];
-  bf16_raw v[2][BC * D];
+  bf16_raw k[SPLIT][2][BC * D];
+  bf16_raw v[SPLIT][2][BC * D];
 };
 
 // LDS tile layout.  Each BC x D bf16 tile is stored densely, row by row,
@@ -156,15 +160,22 @@ __device__ __forceinline__ void tile_scores(f32x16 (&s)[FwdTile<D>::BC / 32], co
   }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+// SPLIT = 1: 4 waves, all keys.  SPLIT = 2 (split-KV inside the workgroup,
+// for grids too small to give every SIMD two waves): 8 waves, waves 4h .. 4h+3
+// take the h-th half of the key tiles for the same 128 query rows, and the
+// two partial (m, l, O) are merged through LDS at the end with the
+// logsumexp identity of "The identity" (FlashAttention: The Matrix You Never
+// Have to Write Down), the same merge Flash-Decoding applies across
+// workgroups ("What it doesn't solve").
+template <int D, bool CAUSAL, int SPLIT>
+__global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c) {
   constexpr int BC = FwdTile<D>::BC;
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NKK = D / 16;    // 16-wide slices of the head dimension
   constexpr int NDB = D / 32;    // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) FwdSmem<D, SPLIT> sm;
 
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
   if (blk >= total) return;
@@ -172,7 +183,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   int qb = blk - bh * n_qblk;
   if (CAUSAL) qb = n_qblk - 1 - qb;  // longest rows first
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (tid >> 6) & (kWaves - 1);  // query wave: rows 32 wave .. + 31
+  const int half = SPLIT == 1 ? 0 : (tid >> 8);  // key range of this wave
   const int g = lane >> 5, col = lane & 31;
   const size_t head = (size_t)bh * N * D;
   const bf16_raw* Qh = Q + head;
@@ -185,6 +198,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   const int kv_end = CAUSAL ? min(N, q_start + kBR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
+  // tiles [t_first, t_end) of this wave's key range; every wave runs n_iter
+  // iterations so that the workgroup barriers line up
+  const int n_iter = (n_tiles + SPLIT - 1) / SPLIT;
+  const int t_first = half * n_iter;
+  const int t_end = min(n_tiles, t_first + n_iter);
 
   TileCopy<D> tc;
   tc.init(wave, lane);
@@ -192,9 +210,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int head_bytes = N * D * 2;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, head_bytes, 0x00020000);
-  // prologue loads: K(0), V(0)
-  issue_tile<D, true>(sm.k[0], krs, 0, tc, wave);
-  issue_tile<D, false>(sm.v[0], vrs, 0, tc, wave);
+  // prologue loads: first K and V tile of the range
+  if (t_first < t_end) {
+    issue_tile<D, true>(sm.k[half][0], krs, t_first * BC, tc, wave);
+    issue_tile<D, false>(sm.v[half][0], vrs, t_first * BC, tc, wave);
+  }
 
   // loop-invariant lane parts of the LDS operand addresses (bytes)
   int kaddr[NKK];
@@ -237,17 +257,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   }
 
   f32x16 s_cur[NKB];
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int it = 0; it < n_iter; ++it) {
+    const int t = t_first + it;
     const int key0 = t * BC;
     // K(t) and V(t) have landed (own loads) and are visible (barrier); every
     // wave is done with tile t-1, whose buffers refill now with tile t+1.
     wait_tile_loads();
     __syncthreads();
-    if (t + 1 < n_tiles) {
-      issue_tile<D, true>(sm.k[(t + 1) & 1], krs, key0 + BC, tc, wave);
-      issue_tile<D, false>(sm.v[(t + 1) & 1], vrs, key0 + BC, tc, wave);
+    if (t >= t_end) continue;  // the shorter key range idles through the barriers
+    if (t + 1 < t_end) {
+      issue_tile<D, true>(sm.k[half][(it + 1) & 1], krs, key0 + BC, tc, wave);
+      issue_tile<D, false>(sm.v[half][(it + 1) & 1], vrs, key0 + BC, tc, wave);
     }
-    tile_scores<D>(s_cur, reinterpret_cast<const char*>(sm.k[t & 1]), kaddr, qf, ak);
+    tile_scores<D>(s_cur, reinterpret_cast<const char*>(sm.k[half][it & 1]), kaddr, qf, ak);
 
     const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > N;
     if (need_mask) {
@@ -313,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     // O^T += V^T P^T, V^T operand via transpose reads of the row-major tile;
     // operand sets rotate per (key block, half) group
-    const char* vtile = reinterpret_cast<const char*>(sm.v[t & 1]);
+    const char* vtile = reinterpret_cast<const char*>(sm.v[half][it & 1]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -336,6 +358,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int db = 0; db < NDB; ++db) pin(av[(grp_i + 1) & 1][db]);
         if (grp_i > 0) pin(pb[(grp_i - 1) >> 1][(grp_i - 1) & 1]);
       }
+  }
+
+  if constexpr (SPLIT == 2) {
+    // merge the second key range into the first: with m = max(m0, m1),
+    // O = 2^(m0-m) O0 + 2^(m1-m) O1 and l = 2^(m0-m) l0 + 2^(m1-m) l1
+    // (a range that saw no key has m = -inf and weight 0)
+    constexpr int NV = NDB * 16 + 3;  // floats per lane: O^T, m, l_run, l_rnd
+    float* xch = reinterpret_cast<float*>(&sm.k[0][0][0]) + (size_t)wave * NV * 64;
+    __syncthreads();  // every wave is done with the tiles
+    if (half == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[(db * 16 + i) * 64 + lane] = oacc[db][i];
+      xch[(NV - 3) * 64 + lane] = m_ref;
+      xch[(NV - 2) * 64 + lane] = l_run;
+      xch[(NV - 1) * 64 + lane] = l_rnd;
+    }
+    __syncthreads();
+    if (half == 1) return;
+    const float m1 = xch[(NV - 3) * 64 + lane];
+    const float m = fmaxf(m_ref, m1);
+    const float a0 = m == -INFINITY ? 0.f : fast_exp2(m_ref - m);
+    const float a1 = m == -INFINITY ? 0.f : fast_exp2(m1 - m);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] = a0 * oacc[db][i] + a1 * xch[(db * 16 + i) * 64 + lane];
+    l_run = a0 * l_run + a1 * xch[(NV - 2) * 64 + lane];
+    l_rnd = a0 * l_rnd + a1 * xch[(NV - 1) * 64 + lane];
+    m_ref = m;
   }
 
   // epilogue: combine the two half-row sums, normalise once, write O and L
@@ -366,9 +419,18 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
   const long long total = (long long)BH * n_qblk;
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
-                     static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
-                     static_cast<const bf16_raw*>(v), o, lse, N, n_qblk, (int)total, scale * kLog2e);
+  // Two 4-wave workgroups per CU keep two waves on every SIMD; a grid too
+  // small for that (fewer than two workgroups per CU) splits each query
+  // block's keys over 8 waves instead.
+  const bool split = total < 2 * kComputeUnits && N > FwdTile<D>::BC;
+  if (split)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2>), dim3(grid), dim3(2 * kThreads), 0, stream,
+                       static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
+                       static_cast<const bf16_raw*>(v), o, lse, N, n_qblk, (int)total, scale * kLog2e);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 1>), dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
+                       static_cast<const bf16_raw*>(v), o, lse, N, n_qblk, (int)total, scale * kLog2e);
   return hipGetLastError();
 }
 

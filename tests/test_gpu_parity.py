@@ -96,6 +96,24 @@ def test_fwd_bf16_ragged(N, d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+def test_fwd_split_and_single_range_paths_agree(d, causal):
+    # A small grid runs the split-key-range kernel (8 waves, two key ranges
+    # merged by the logsumexp identity); the same heads repeated into a grid
+    # of >= 2 workgroups per CU run the 4-wave kernel.  Both against the oracle.
+    N = 1000
+    t = shape_inputs(1, 2, N, d, "bf16", 700 + d)
+    say(f"fwd split vs single-range d={d} causal={causal}")
+    o_small, l_small = run_fwd(t, causal)
+    big = {n: t[n].repeat(1, 128, 1, 1) for n in ("q", "k", "v")}  # 256 heads, 2048 workgroups
+    o_big, l_big = run_fwd(big, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(d))
+    check_fwd(o_small, l_small, oref, lref, f"split d={d} causal={causal}")
+    check_fwd(o_big[:, :2], l_big[:, :2], oref, lref, f"single-range d={d} causal={causal}")
+    assert np.array_equal(o_big[:, :2], o_big[:, 2:4])  # identical heads, identical results
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 37, 129, 300])
 def test_fwd_f32_ragged(N, d, causal):
     t = shape_inputs(2, 1, N, d, "f32", 200 + N + d)
