@@ -1,7 +1,8 @@
 """Throughput of the exact-attention hot path on one MI355X.
 
-A step is one pass of the whole path -- fa_fwd then fa_bwd (D preprocess and
-the recompute backward) -- over the forward+backward workload
+A step is one pass of the whole path -- fa_fwd then fa_bwd (per-row
+preprocess, the key-stationary dK/dV pass, the query-stationary dQ pass) --
+over the forward+backward workload
 B=2, H=16, N=4096, d=128, causal, bf16 Q/K/V/dO ~ N(0,1), with inputs resident
 in device memory before the timed region.  ``value`` is attention TFLOP/s of
 the step: 3.5 * (4*B*H*N^2*d / 2) FLOP per step (forward counted as
@@ -10,9 +11,11 @@ the step: 3.5 * (4*B*H*N^2*d / 2) FLOP per step (forward counted as
 Also reported on the same line:
   fwd        forward alone on B=1, H=8, N=4096, d=128, non-causal
   phases     forward and backward of the step timed separately
-  roofline   the dominant kernel (the backward's main kernel) against the
-             bf16 matrix-core peak; traffic from committed rocprofv3 counters
-             when they were taken on the current kernel sources
+  kernels    each kernel of the step timed alone through its C entry point
+             (fa_fwd, fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq)
+  roofline   the dominant kernel of the step against the bf16 matrix-core
+             peak; traffic from committed rocprofv3 counters when they were
+             taken on the current kernel sources
   cpu_baseline  the float64 oracle on a bounded sample of the workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -150,7 +153,33 @@ def main():
     ms_fwd = time_calls(fwd, args.steps, stream)
     ms_bwd = time_calls(bwd, args.steps, stream)
     bwd_tflops = 2.5 * w.fwd_flop() / (ms_bwd * 1e-3) / 1e12
-    traffic, traffic_src = committed_traffic("bwd_main_d128_causal")
+
+    # each kernel of the step alone (workspace prepared once for the two passes)
+    dq_o, dk_o, dv_o = (torch.empty_like(o) for _ in range(3))
+    fa.backward_prep(o, lse, do, ws)
+    torch.cuda.synchronize()
+    F = w.fwd_flop()
+    kernels = {
+        # name: (call, counter key, algorithmic FLOP, executed FLOP)
+        "fa_fwd": (fwd, "fwd_d128_causal", F, F),
+        "fa_bwd_prep": (lambda: fa.backward_prep(o, lse, do, ws), "bwd_pre_d128", 0.0, 0.0),
+        "fa_bwd_dkdv": (lambda: fa.backward_dkdv(q, k, v, do, ws, causal=True, dk=dk_o, dv=dv_o),
+                        "bwd_dkdv_d128_causal", 2.0 * F, 2.0 * F),
+        "fa_bwd_dq": (lambda: fa.backward_dq(q, k, v, do, ws, causal=True, dq=dq_o),
+                      "bwd_dq_d128_causal", 0.5 * F, 1.5 * F),
+    }
+    kern = {}
+    for name, (fn, key, flop, xflop) in kernels.items():
+        for _ in range(3):
+            fn()
+        ms_k = time_calls(fn, args.steps, stream)
+        kern[name] = {"ms": round(ms_k, 4), "counter_key": key,
+                      "algorithmic_tflops": round(flop / (ms_k * 1e-3) / 1e12, 2) if flop else None,
+                      "executed_tflops": round(xflop / (ms_k * 1e-3) / 1e12, 2) if xflop else None}
+    dom = max(kern, key=lambda n: kern[n]["ms"])
+    dom_flop = kernels[dom][2]
+    dom_ach = dom_flop / (kern[dom]["ms"] * 1e-3) / 1e12
+    traffic, traffic_src = committed_traffic(kern[dom]["counter_key"])
 
     # ------------------------------------------------------------ forward headline workload
     wf = I.FWD_4K_D128
@@ -166,7 +195,7 @@ def main():
         fwd2()
     ms_f2 = time_calls(fwd2, args.steps, stream)
     f2 = wf.fwd_flop() / (ms_f2 * 1e-3) / 1e12
-    f2_traffic, f2_src = committed_traffic("fwd_d128")
+    f2_traffic, f2_src = committed_traffic("fwd_d128_split2")
 
     res = {
         "metric": "attention TFLOP/s (fwd, fwd+bwd) bf16 at 1 MI355X; % of MFMA peak",
@@ -195,23 +224,24 @@ def main():
             "bwd_ms": round(ms_bwd, 4),
             "bwd_tflops": round(bwd_tflops, 2),
         },
+        "kernels": kern,
         "roofline": {
-            "kernel": "bwd_main_kernel<128, causal> (timed as the fa_bwd call, which adds the small D preprocess)",
+            "kernel": f"{dom} ({kern[dom]['counter_key']}), timed alone with HIP events on its launch stream",
             "bound": "mfma",
-            "achieved": round(bwd_tflops, 2),
+            "achieved": round(dom_ach, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(dom_ach / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "traffic_source": traffic_src,
-            "algorithmic_flop_per_launch": 2.5 * w.fwd_flop(),
+            "algorithmic_flop_per_launch": dom_flop,
         },
         "fwd": {
             "workload": wf.name,
             "ms": round(ms_f2, 4),
             "tflops": round(f2, 2),
             "roofline": {
-                "kernel": "fwd_bf16_kernel<128, non-causal>",
+                "kernel": "fwd_bf16_kernel<128, non-causal, split-KV x2> (the launch this grid gets)",
                 "bound": "mfma",
                 "achieved": round(f2, 2),
                 "peak": PEAK_BF16_TFLOPS,

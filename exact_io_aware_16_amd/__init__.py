@@ -17,7 +17,8 @@ import os
 
 import torch
 
-__all__ = ["forward", "backward", "library", "FAError", "LIB_PATH", "status_string"]
+__all__ = ["forward", "backward", "backward_prep", "backward_dkdv", "backward_dq", "library", "FAError",
+           "LIB_PATH", "status_string"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -49,6 +50,12 @@ def library():
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd.restype = i
+        lib.fa_bwd_prep.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp]
+        lib.fa_bwd_prep.restype = i
+        lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd_dkdv.restype = i
+        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd_dq.restype = i
         lib.fa_status_string.argtypes = [i]
         lib.fa_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -118,12 +125,7 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
     return o, l
 
 
-def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
-    """Gradients (dQ, dK, dV), float32 [B,H,N,d], of sum(dO * O).
-
-    ``o`` and ``lse`` must be the forward's outputs for the same inputs; the
-    probability tiles are recomputed from them.  bf16 inputs only.
-    """
+def _check_bwd(q, k, v, o, lse, do):
     _check(q, k, v)
     if q.dtype != torch.bfloat16 or do.dtype != torch.bfloat16:
         raise TypeError("backward takes bfloat16 Q, K, V and dO")
@@ -135,18 +137,91 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
         raise ValueError("dO, O and L must be contiguous")
     if not (do.device == o.device == lse.device == q.device):
         raise ValueError("all tensors must be on the same device")
+
+
+def _out(t, like):
+    """A float32 output of Q's shape: a new tensor, or the given one after checks."""
+    if t is None:
+        return torch.empty(like.shape, dtype=torch.float32, device=like.device)
+    if t.dtype != torch.float32 or t.shape != like.shape or t.device != like.device or not t.is_contiguous():
+        raise ValueError("outputs must be contiguous float32 tensors of Q's shape on Q's device")
+    return t
+
+
+def workspace_for(q, workspace=None):
+    """The backward workspace for Q's shape: the given one (checked) or a new one."""
     B, H, N, d = q.shape
-    lib = library()
-    ws_bytes = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    ws_bytes = library().fa_bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
-        workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=q.device)
-    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        return torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on Q's device")
+    if workspace.numel() * workspace.element_size() < ws_bytes:
         raise ValueError(f"workspace too small: need {ws_bytes} bytes")
+    return workspace
+
+
+def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
+    """Gradients (dQ, dK, dV), float32 [B,H,N,d], of sum(dO * O).
+
+    ``o`` and ``lse`` must be the forward's outputs for the same inputs; the
+    probability tiles are recomputed from them.  bf16 inputs only.
+    """
+    _check_bwd(q, k, v, o, lse, do)
+    B, H, N, d = q.shape
+    workspace = workspace_for(q, workspace)
     dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
-    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-                    _ptr(workspace), B, H, N, d, _scale(scale, d), int(bool(causal)), _stream(q.device))
+    st = library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(workspace), B, H, N, d, _scale(scale, d), int(bool(causal)), _stream(q.device))
     if st != FA_OK:
         raise FAError("fa_bwd", st)
     return dq, dk, dv
+
+
+def backward_prep(o, lse, do, workspace, scale=None):
+    """First backward phase: per-row scale * (dO . O) and L log2(e) into ``workspace``."""
+    if do.dtype != torch.bfloat16 or o.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise TypeError("dO bfloat16, O and L float32")
+    if do.ndim != 4 or o.shape != do.shape or lse.shape != do.shape[:3]:
+        raise ValueError("dO and O must be [B, H, N, d] and L [B, H, N]")
+    if not (do.is_contiguous() and o.is_contiguous() and lse.is_contiguous()):
+        raise ValueError("dO, O and L must be contiguous")
+    B, H, N, d = do.shape
+    workspace = workspace_for(do, workspace)
+    st = library().fa_bwd_prep(_ptr(do), _ptr(o), _ptr(lse), _ptr(workspace), B, H, N, d, _scale(scale, d),
+                               _stream(do.device))
+    if st != FA_OK:
+        raise FAError("fa_bwd_prep", st)
+    return workspace
+
+
+def backward_dkdv(q, k, v, do, workspace, causal=False, scale=None, dk=None, dv=None):
+    """Second backward phase: (dK, dV) from a workspace filled by backward_prep."""
+    _check(q, k, v)
+    if q.dtype != torch.bfloat16 or do.dtype != torch.bfloat16 or do.shape != q.shape:
+        raise TypeError("bfloat16 Q, K, V and dO of one shape")
+    B, H, N, d = q.shape
+    workspace = workspace_for(q, workspace)
+    dk, dv = _out(dk, q), _out(dv, q)
+    st = library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace), _ptr(dk), _ptr(dv), B, H, N, d,
+                               _scale(scale, d), int(bool(causal)), _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_bwd_dkdv", st)
+    return dk, dv
+
+
+def backward_dq(q, k, v, do, workspace, causal=False, scale=None, dq=None):
+    """Third backward phase: dQ from a workspace filled by backward_prep."""
+    _check(q, k, v)
+    if q.dtype != torch.bfloat16 or do.dtype != torch.bfloat16 or do.shape != q.shape:
+        raise TypeError("bfloat16 Q, K, V and dO of one shape")
+    B, H, N, d = q.shape
+    workspace = workspace_for(q, workspace)
+    dq = _out(dq, q)
+    st = library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace), _ptr(dq), B, H, N, d,
+                             _scale(scale, d), int(bool(causal)), _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_bwd_dq", st)
+    return dq

@@ -31,6 +31,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 COPY_BYTES = 512 << 20
 REPEAT = 5
+# the SQ counter group of the summary (eight SQ counters fit one pass)
+SQ_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES "
+               "SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_ANY SQ_WAVE_CYCLES")
 
 
 def kernel_source_digest():
@@ -46,14 +49,15 @@ def kernel_source_digest():
 
 def kernel_key(name):
     """Short key for a (possibly mangled) kernel name, or None."""
-    m = re.search(r"fwd_bf16_kernel(?:ILi|<)(\d+)(?:ELb|, )(\d|true|false)", name)
+    m = re.search(r"fwd_bf16_kernel(?:ILi|<)(\d+)(?:ELb|, )(\d|true|false)(?:ELi|, )(\d)", name)
     if m:
         causal = m.group(2) in ("1", "true")
-        return f"fwd_d{m.group(1)}" + ("_causal" if causal else "")
-    m = re.search(r"bwd_main_kernel(?:ILi|<)(\d+)(?:ELb|, )(\d|true|false)", name)
-    if m:
-        causal = m.group(2) in ("1", "true")
-        return f"bwd_main_d{m.group(1)}" + ("_causal" if causal else "")
+        return f"fwd_d{m.group(1)}" + ("_causal" if causal else "") + ("_split2" if m.group(3) == "2" else "")
+    for kern, short in (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq")):
+        m = re.search(kern + r"(?:ILi|<)(\d+)(?:ELb|, )(\d|true|false)", name)
+        if m:
+            causal = m.group(2) in ("1", "true")
+            return f"{short}_d{m.group(1)}" + ("_causal" if causal else "")
     m = re.search(r"bwd_pre_kernel(?:ILi|<)(\d+)", name)
     if m:
         return f"bwd_pre_d{m.group(1)}"
@@ -72,6 +76,8 @@ def run():
     from exact_io_aware_16_amd import inputs as I
 
     dev = torch.device("cuda:0")
+    # the forward workload (its grid takes the split-KV launch) and the
+    # forward+backward workload (every kernel of the step)
     for w in (I.FWD_4K_D128, I.FWDBWD_4K_D128):
         t = I.make_inputs(w)
         q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
@@ -166,16 +172,25 @@ def summarize(args):
     print(json.dumps(rec, indent=1, sort_keys=True))
 
 
+_F5 = 2.0 * 32 * 4096 ** 2 * 128  # forward FLOP of B=2 H=16 N=4096 d=128 causal (two products)
 ALGORITHMIC = {
-    # key: (workload, algorithmic HBM bytes per launch, algorithmic FLOP per launch)
-    "fwd_d128": ("B=1 H=8 N=4096 d=128 non-causal", 3 * 8 * 4096 * 128 * 2 + 8 * 4096 * 128 * 4 + 8 * 4096 * 4,
-                 4.0 * 8 * 4096 ** 2 * 128),
+    # key: (workload, algorithmic HBM bytes per launch, algorithmic FLOP per launch,
+    #       FLOP the kernel executes per launch)
+    "fwd_d128_split2": ("B=1 H=8 N=4096 d=128 non-causal",
+                        3 * 8 * 4096 * 128 * 2 + 8 * 4096 * 128 * 4 + 8 * 4096 * 4,
+                        4.0 * 8 * 4096 ** 2 * 128, 4.0 * 8 * 4096 ** 2 * 128),
     "fwd_d128_causal": ("B=2 H=16 N=4096 d=128 causal", 3 * 32 * 4096 * 128 * 2 + 32 * 4096 * 128 * 4 + 32 * 4096 * 4,
-                        2.0 * 32 * 4096 ** 2 * 128),
-    "bwd_pre_d128": ("B=2 H=16 N=4096 d=128", 32 * 4096 * 128 * (2 + 4 + 4) + 32 * 4096 * 4 * 3, 0.0),
-    "bwd_main_d128_causal": ("B=2 H=16 N=4096 d=128 causal",
-                             4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 3 * 32 * 4096 * 128 * 4,
-                             2.5 * 2.0 * 32 * 4096 ** 2 * 128),
+                        _F5, _F5),
+    # reads dO (bf16), O and L (float32); writes scale*D and L log2(e)
+    "bwd_pre_d128": ("B=2 H=16 N=4096 d=128", 32 * 4096 * 128 * (2 + 4) + 32 * 4096 * 4 * 3, 0.0, 0.0),
+    # reads Q, K, V, dO and the two workspace floats per row; writes dK, dV.
+    # S, dP, dV, dK: four of the backward's five products
+    "bwd_dkdv_d128_causal": ("B=2 H=16 N=4096 d=128 causal",
+                             4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 2 * 32 * 4096 * 128 * 4, 2.0 * _F5, 2.0 * _F5),
+    # reads Q, K, V, dO and the workspace; writes dQ.  dQ is the fifth product;
+    # S and dP are computed a second time (1.5x the forward executed)
+    "bwd_dq_d128_causal": ("B=2 H=16 N=4096 d=128 causal",
+                           4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 32 * 4096 * 128 * 4, 0.5 * _F5, 1.5 * _F5),
 }
 
 
@@ -189,8 +204,7 @@ def markdown_counters(rec, args):
            "cd /tmp && export TMPDIR=/tmp PYTHONPATH=$REPO",
            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o run -- python -u -m exact_io_aware_16_amd.counters run",
            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o run -- python -u -m exact_io_aware_16_amd.counters run",
-           "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES "
-           "SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU --output-format csv -d $OUT/pmc_sq -o run -- python -u -m exact_io_aware_16_amd.counters run",
+           f"rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d $OUT/pmc_sq -o run -- python -u -m exact_io_aware_16_amd.counters run",
            "python -m exact_io_aware_16_amd.counters summarize --fetch $OUT/pmc_fetch --write $OUT/pmc_write --sq $OUT/pmc_sq --stats $OUT/prof_stats",
            "```", "",
            f"Kernel-source digest: `{rec['source_sha256'][:16]}`.", "",
@@ -201,7 +215,7 @@ def markdown_counters(rec, args):
            "| kernel | workload | fetch MiB | write MiB | HBM MiB | algorithmic MiB | ratio |",
            "|---|---|---|---|---|---|---|"]
     for k, v in sorted(rec["kernels"].items()):
-        wl, alg, _ = ALGORITHMIC.get(k, ("", 0, 0))
+        wl, alg, _, _ = ALGORITHMIC.get(k, ("", 0, 0, 0))
         ratio = f"{v['hbm_bytes_per_launch'] / alg:.2f}" if alg else ""
         out.append(f"| {k} | {wl} | {v['fetch_bytes'] / 2**20:.1f} | {v['write_bytes'] / 2**20:.1f} | "
                    f"{v['hbm_bytes_per_launch'] / 2**20:.1f} | {alg / 2**20:.1f} | {ratio} |")
@@ -215,7 +229,10 @@ def markdown_counters(rec, args):
                 continue
             out.append(f"| {k} | " + " | ".join(f"{d.get(n, 0):.0f}" for n in names) + " |")
         out += ["", "SQ_VALU_MFMA_BUSY_CYCLES counts 32 per 32x32x16 bf16 MFMA summed over all SIMDs;",
-                "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE is the fraction of LDS cycles lost to conflicts."]
+                "SQ_VALU_MFMA_COEXEC_CYCLES counts cycles where a vector instruction issued while the matrix",
+                "core was busy; SQ_WAIT_ANY / SQ_WAVE_CYCLES (both in quad-cycles) is the share of wave time",
+                "spent waiting on dependencies; SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE is the fraction of",
+                "LDS cycles lost to conflicts."]
     out.append("")
     return "\n".join(out)
 
@@ -227,15 +244,18 @@ def markdown_stats(stats, args):
            "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_stats -o run -- "
            "python -u $REPO/bench.py --no-cpu-baseline --steps 20 --warmup 5",
            "```", "",
-           "The bench runs the fwd+bwd step (B=2,H=16,N=4096,d=128 causal), then forward and backward",
-           "alone on the same inputs, then the forward workload B=1,H=8,N=4096,d=128.", "",
-           "| kernel | calls | average us | min us | max us | TFLOP/s at average |",
-           "|---|---|---|---|---|---|"]
+           "The bench runs the fwd+bwd step (B=2,H=16,N=4096,d=128 causal), then each of its kernels",
+           "alone on the same inputs, then the forward workload B=1,H=8,N=4096,d=128.",
+           "Algorithmic TFLOP/s counts the attention products the method needs (forward 2, backward 5);",
+           "executed TFLOP/s counts what the kernel runs (the dQ kernel recomputes S and dP).", "",
+           "| kernel | calls | average us | min us | max us | algorithmic TFLOP/s | executed TFLOP/s |",
+           "|---|---|---|---|---|---|---|"]
     for k, v in sorted(stats.items()):
-        flop = ALGORITHMIC.get(k, ("", 0, 0))[2]
+        _, _, flop, xflop = ALGORITHMIC.get(k, ("", 0, 0, 0))
         tf = f"{flop / (v['avg_ns'] * 1e-9) / 1e12:.1f}" if flop else ""
+        xtf = f"{xflop / (v['avg_ns'] * 1e-9) / 1e12:.1f}" if xflop else ""
         out.append(f"| {k} | {v['calls']} | {v['avg_ns'] / 1e3:.1f} | {v['min_ns'] / 1e3:.1f} | "
-                   f"{v['max_ns'] / 1e3:.1f} | {tf} |")
+                   f"{v['max_ns'] / 1e3:.1f} | {tf} | {xtf} |")
     out.append("")
     return "\n".join(out)
 

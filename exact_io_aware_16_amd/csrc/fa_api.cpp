@@ -79,6 +79,45 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const fl
                                         N, d, scale, causal, stream));
 }
 
+int fa_bwd_prep(const void* dout, const float* o, const float* lse, void* workspace, int B, int H, int N, int d,
+                float scale, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, 0, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!dout || !o || !lse) return FA_ERR_NULL;
+  if (!workspace) return FA_ERR_WORKSPACE;
+  return hip_status(fa::launch_bwd_prep(dout, o, lse, static_cast<float*>(workspace), B * H, N, d, scale, stream));
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const void* workspace, float* dk,
+                float* dv, int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !dout || !dk || !dv) return FA_ERR_NULL;
+  if (!workspace) return FA_ERR_WORKSPACE;
+  return hip_status(fa::launch_bwd_dkdv(q, k, v, dout, static_cast<const float*>(workspace), dk, dv, B * H, N, d,
+                                        scale, causal, stream));
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const void* workspace, float* dq,
+              int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !dout || !dq) return FA_ERR_NULL;
+  if (!workspace) return FA_ERR_WORKSPACE;
+  const float* ws = static_cast<const float*>(workspace);
+  const size_t rows = (size_t)B * (size_t)H * (size_t)N;
+  return hip_status(fa::launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, B * H, N, d, scale, causal, stream));
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -398,40 +398,58 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
-                  float* dq, float* dk, float* dv, float* ws, int BH, int N, float scale, hipStream_t stream) {
+template <int D>
+hipError_t launch_prep(const void* dout, const float* o, const float* lse, float* ws, int BH, int N, float scale,
+                       hipStream_t stream) {
   const long long rows = (long long)BH * N;
   constexpr int RPB = 256 / (D / 8);
   const long long pre_grid = (rows + RPB - 1) / RPB;
+  if (pre_grid > (1LL << 31) - 1) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_grid), dim3(256), 0, stream,
+                     static_cast<const bf16_raw*>(dout), o, lse, ws, ws + rows, rows, scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws, float* dk,
+                       float* dv, int BH, int N, float scale, hipStream_t stream) {
+  const long long rows = (long long)BH * N;
   const int n_kvblk = (N + kBKV - 1) / kBKV;
   const long long total = (long long)BH * n_kvblk;
-  if (pre_grid > (1LL << 31) - 1 || total > (1LL << 30)) return hipErrorInvalidConfiguration;
-  float* dsc = ws;
-  float* l2 = ws + rows;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_grid), dim3(256), 0, stream,
-                     static_cast<const bf16_raw*>(dout), o, lse, dsc, l2, rows, scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k), static_cast<const bf16_raw*>(v),
-                     static_cast<const bf16_raw*>(dout), l2, dsc, dk, dv, N, n_kvblk, (int)total, scale,
+                     static_cast<const bf16_raw*>(dout), ws + rows, ws, dk, dv, N, n_kvblk, (int)total, scale,
                      scale * kLog2e);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq_bf16(q, k, v, dout, l2, dsc, dq, BH, N, D, scale, CAUSAL ? 1 : 0, stream);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_bwd_prep(const void* dout, const float* o, const float* lse, float* ws, int BH, int N, int d,
+                           float scale, hipStream_t stream) {
+  return d == 128 ? launch_prep<128>(dout, o, lse, ws, BH, N, scale, stream)
+                  : launch_prep<64>(dout, o, lse, ws, BH, N, scale, stream);
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws,
+                           float* dk, float* dv, int BH, int N, int d, float scale, int causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch_dkdv<128, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, stream)
+                              : launch_dkdv<128, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, stream);
+  return causal ? launch_dkdv<64, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, stream)
+                : launch_dkdv<64, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, stream);
+}
+
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* ws, int BH, int N, int d,
                            float scale, int causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch<128, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, scale, stream)
-                              : launch<128, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, scale, stream);
-  return causal ? launch<64, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, scale, stream)
-                : launch<64, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, scale, stream);
+  hipError_t e = launch_bwd_prep(dout, o, lse, ws, BH, N, d, scale, stream);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, N, d, scale, causal, stream);
+  if (e != hipSuccess) return e;
+  const long long rows = (long long)BH * N;
+  return launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, BH, N, d, scale, causal, stream);
 }
 
 }  // namespace fa

@@ -19,6 +19,13 @@ hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const
                               const float* dsc, float* dq, int BH, int N, int d, float scale, int causal,
                               hipStream_t stream);
 
+// Backward phases (fa_bwd.hip); ws holds [scale * D | L log2(e)], BH * N
+// floats each.
+hipError_t launch_bwd_prep(const void* dout, const float* o, const float* lse, float* ws, int BH, int N, int d,
+                           float scale, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws,
+                           float* dk, float* dv, int BH, int N, int d, float scale, int causal, hipStream_t stream);
+
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* dvec, int BH, int N,
                            int d, float scale, int causal, hipStream_t stream);

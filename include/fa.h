@@ -105,6 +105,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const fl
            const void* dout, float* dq, float* dk, float* dv, void* workspace,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
+/*
+ * The three phases fa_bwd runs, for callers that schedule or time them
+ * separately (same arguments, layouts and errors as fa_bwd; workspace as
+ * sized by fa_bwd_workspace_bytes).  fa_bwd(...) is exactly
+ *   fa_bwd_prep(...); fa_bwd_dkdv(...); fa_bwd_dq(...);
+ * on one stream, and the results are bitwise the same.
+ *
+ * fa_bwd_prep: per query row, scale * (dO_i . O_i) and L_i log2(e) into the
+ *   workspace.  Reads dout, o, lse.
+ * fa_bwd_dkdv: dK and dV, one pass per block of 128 keys over the query
+ *   rows (causal: from the block's diagonal on).  Reads q, k, v, dout and
+ *   the prepared workspace.
+ * fa_bwd_dq: dQ, one pass per block of 128 query rows over the key tiles it
+ *   sees, recomputing the probability tiles.  Reads q, k, v, dout and the
+ *   prepared workspace.
+ */
+int fa_bwd_prep(const void* dout, const float* o, const float* lse, void* workspace,
+                int B, int H, int N, int d, float scale, hipStream_t stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const void* workspace,
+                float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+                hipStream_t stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const void* workspace,
+              float* dq, int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
 /* Static, human-readable text for an fa_status value (never NULL). */
 const char* fa_status_string(int status);
 

@@ -247,6 +247,22 @@ def test_bwd_ragged(N, d, causal):
     check_bwd(got, oracle_bwd(t, causal, 1 / math.sqrt(d)), f"bwd N={N} d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_bwd_phases_compose_to_fa_bwd(d, causal):
+    # fa_bwd is fa_bwd_prep; fa_bwd_dkdv; fa_bwd_dq on one stream: bitwise equal
+    t = shape_inputs(1, 2, 300, d, "bf16", 500 + d, with_do=True)
+    q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
+    say(f"bwd phases d={d} causal={causal}")
+    o, l = fa.forward(q, k, v, causal=causal)
+    dq, dk, dv = fa.backward(q, k, v, o, l, do, causal=causal)
+    ws = fa.backward_prep(o, l, do, None)
+    dk2, dv2 = fa.backward_dkdv(q, k, v, do, ws, causal=causal)
+    dq2 = fa.backward_dq(q, k, v, do, ws, causal=causal)
+    torch.cuda.synchronize()
+    for a_, b_ in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a_, b_)
+
+
 def test_fwdbwd_4k_d128_causal_full():
     w = I.FWDBWD_4K_D128
     t = I.make_inputs(w)
