@@ -7,8 +7,9 @@ outputs with torch on the inputs' device and passes raw device pointers and
 the current HIP stream.  Every arithmetic step runs in the library's
 kernels; there is no fallback.  If libfa.so has not been built this raises.
 
-    o, lse = forward(q, k, v, causal=False)          # q,k,v: [B,H,N,d] bf16 or f32
-    dq, dk, dv = backward(q, k, v, o, lse, do, causal=False)
+    o, lse = forward(q, k, v, causal=False)     # q [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,dv]
+    o, lse = forward_splitkv(q, k, v)            # same result, keys split over workgroups
+    dq, dk, dv = backward(q, k, v, o, lse, do, causal=False)   # [B,H,N,d] each
 """
 
 import ctypes
@@ -17,7 +18,7 @@ import os
 
 import torch
 
-__all__ = ["forward", "backward", "backward_prep", "backward_dkdv", "backward_dq", "library", "FAError",
+__all__ = ["forward", "forward_splitkv", "backward", "backward_prep", "backward_dkdv", "backward_dq", "library", "FAError",
            "LIB_PATH", "status_string"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -46,6 +47,12 @@ def library():
         lib.fa_fwd.restype = i
         lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_fwd_f32.restype = i
+        lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        lib.fa_fwd_ex.restype = i
+        lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        lib.fa_fwd_splitkv.restype = i
         lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
@@ -66,8 +73,12 @@ def status_string(status):
     return library().fa_status_string(int(status)).decode()
 
 
-def _check(q, k, v):
-    """Input contract: the page's single-head checks, extended to [B, H, N, d]."""
+def _check(q, k, v, square=True):
+    """Input contract: the page's single-head checks, extended to [B, H, N, d].
+
+    square=False admits the page's general shapes, Q [B,H,Nq,d], K [B,H,Nk,d],
+    V [B,H,Nk,dv]; square=True also requires Nq == Nk and dv == d.
+    """
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("Q, K, V must be rank 4 [B, H, N, d]")
     if not all(t.is_floating_point() for t in (q, k, v)):
@@ -84,7 +95,11 @@ def _check(q, k, v):
         raise ValueError("query/key width must be positive")
     if not (q.device == k.device == v.device):
         raise ValueError("Q, K, V must be on the same device")
-    if q.shape != k.shape or k.shape != v.shape:
+    if q.shape[:2] != k.shape[:2] or k.shape[:2] != v.shape[:2]:
+        raise ValueError(f"batch and head counts differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if v.shape[-1] == 0:
+        raise ValueError("value width must be positive")
+    if square and (q.shape != k.shape or k.shape != v.shape):
         raise ValueError(f"Q, K, V must share one [B, H, N, d] shape, got {tuple(q.shape)}, "
                          f"{tuple(k.shape)}, {tuple(v.shape)}")
     if q.device.type != "cuda":
@@ -105,23 +120,67 @@ def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
+def _outputs(q, v, out, lse):
+    B, H, Nq = q.shape[:3]
+    dv = v.shape[-1]
+    o = out if out is not None else torch.empty((B, H, Nq, dv), dtype=torch.float32, device=q.device)
+    l = lse if lse is not None else torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if o.shape != (B, H, Nq, dv) or l.shape != (B, H, Nq) or o.dtype != torch.float32 or l.dtype != torch.float32:
+        raise ValueError("out must be float32 [B, H, Nq, dv] and lse float32 [B, H, Nq]")
+    if not (o.is_contiguous() and l.is_contiguous()) or o.device != q.device or l.device != q.device:
+        raise ValueError("out and lse must be contiguous and on Q's device")
+    return o, l
+
+
 def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
-    """Exact attention: returns (O float32 [B,H,N,d], L float32 [B,H,N]).
+    """Exact attention: returns (O float32 [B,H,Nq,dv], L float32 [B,H,Nq]).
 
     L is the natural-log logsumexp of the scaled, masked scores of each row.
-    bf16 inputs run the matrix-core kernel (fa_fwd); float32 inputs run the
-    float32 kernel (fa_fwd_f32).  ``out``/``lse`` may be preallocated.
+    bf16 inputs run the matrix-core kernel (fa_fwd for one shared [B,H,N,d]
+    shape, fa_fwd_ex for Nq != Nk or dv != d); float32 inputs run the float32
+    kernel (fa_fwd_f32, one shared shape).  Causal masking is upper-left.
+    ``out``/``lse`` may be preallocated.
     """
-    _check(q, k, v)
-    B, H, N, d = q.shape
-    o = out if out is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-    l = lse if lse is not None else torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(q, k, v, square=q.dtype != torch.bfloat16)
+    B, H, Nq, d = q.shape
+    Nk, dv = k.shape[2], v.shape[3]
+    o, l = _outputs(q, v, out, lse)
     lib = library()
-    fn = lib.fa_fwd if q.dtype == torch.bfloat16 else lib.fa_fwd_f32
-    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d, _scale(scale, d), int(bool(causal)),
-            _stream(q.device))
+    sc, cz, stream = _scale(scale, d), int(bool(causal)), _stream(q.device)
+    if q.dtype == torch.float32:
+        name, st = "fa_fwd_f32", lib.fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, Nq, d, sc, cz,
+                                                stream)
+    elif Nq == Nk and dv == d:
+        name, st = "fa_fwd", lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, Nq, d, sc, cz, stream)
+    else:
+        name, st = "fa_fwd_ex", lib.fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, Nq, Nk, d, dv, sc,
+                                              cz, stream)
     if st != FA_OK:
-        raise FAError("fa_fwd" if q.dtype == torch.bfloat16 else "fa_fwd_f32", st)
+        raise FAError(name, st)
+    return o, l
+
+
+def forward_splitkv(q, k, v, causal=False, scale=None, n_splits=0, workspace=None, out=None, lse=None):
+    """Split-KV forward (fa_fwd_splitkv): the same result as forward() for
+    bf16 inputs, with the key tiles cut into ``n_splits`` ranges handled by
+    separate workgroups and merged by logsumexp (0: chosen for the grid).
+    Meant for few query rows against long key sequences (decoding)."""
+    _check(q, k, v, square=False)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the split-KV forward takes bfloat16 Q, K, V")
+    B, H, Nq, d = q.shape
+    Nk, dv = k.shape[2], v.shape[3]
+    o, l = _outputs(q, v, out, lse)
+    lib = library()
+    need = lib.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dv, int(n_splits))
+    if workspace is None:
+        workspace = torch.empty((max(need, 4),), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need or workspace.device != q.device:
+        raise ValueError(f"workspace must hold {need} bytes on Q's device")
+    st = lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _ptr(workspace), B, H, Nq, Nk, d, dv,
+                            _scale(scale, d), int(bool(causal)), int(n_splits), _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_fwd_splitkv", st)
     return o, l
 
 

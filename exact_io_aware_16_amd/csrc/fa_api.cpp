@@ -29,6 +29,22 @@ int check_shape(int B, int H, int N, int d, int causal, bool* empty) {
   return FA_OK;
 }
 
+// Shapes of the general forward: Q [B,H,Nq,d], K [B,H,Nk,d], V [B,H,Nk,dv].
+int check_shape_ex(int B, int H, int Nq, int Nk, int d, int dv, int causal, bool* empty) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d) || !head_dim_ok(dv)) return FA_ERR_HEADDIM;
+  *empty = (B == 0 || H == 0 || Nq == 0);
+  const long long bh = (long long)B * H;
+  if (bh > INT32_MAX) return FA_ERR_SHAPE;
+  if ((double)bh * Nq * dv > 4.0e18 || (double)bh * Nk * (d + dv) > 4.0e18) return FA_ERR_SHAPE;
+  // per-head byte ranges of the buffer descriptors stay below 2^31
+  if ((long long)Nq * dv * 4 > INT32_MAX || (long long)Nk * d * 2 > INT32_MAX ||
+      (long long)Nk * dv * 2 > INT32_MAX)
+    return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
@@ -45,7 +61,42 @@ int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, in
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, scale, causal, stream));
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, scale, stream));
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int Nq, int Nk, int d,
+              int dv, float scale, int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape_ex(B, H, Nq, Nk, d, dv, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!o || !lse || (Nk > 0 && (!q || !k || !v))) return FA_ERR_NULL;
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, scale, stream));
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dv, int n_splits) {
+  bool empty = false;
+  if (check_shape_ex(B, H, Nq, Nk, d, dv, 0, &empty) != FA_OK || empty) return 0;
+  if (n_splits < 0 || n_splits > 256) return 0;
+  const int n = fa::fwd_splitkv_resolve(B * H, Nq, Nk, d, dv, n_splits);
+  if (n <= 1) return 0;
+  return (size_t)n * (size_t)B * (size_t)H * (size_t)Nq * (size_t)(dv + 1) * sizeof(float);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float* lse, void* workspace, int B, int H,
+                   int Nq, int Nk, int d, int dv, float scale, int causal, int n_splits, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape_ex(B, H, Nq, Nk, d, dv, causal, &empty);
+  if (st != FA_OK) return st;
+  if (n_splits < 0 || n_splits > 256) return FA_ERR_SHAPE;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!o || !lse || (Nk > 0 && (!q || !k || !v))) return FA_ERR_NULL;
+  const int n = fa::fwd_splitkv_resolve(B * H, Nq, Nk, d, dv, n_splits);
+  if (n > 1 && !workspace) return FA_ERR_WORKSPACE;
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, n,
+                                        static_cast<float*>(workspace), scale, stream));
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
@@ -125,7 +176,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "invalid shape (negative B/H/N, causal not 0/1, or size overflow)";
     case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
-    case FA_ERR_WORKSPACE: return "backward workspace is NULL";
+    case FA_ERR_WORKSPACE: return "workspace is NULL";
     case FA_ERR_HIP: return "HIP runtime rejected a kernel launch";
     default: return "unknown fa_status";
   }

@@ -15,6 +15,10 @@
 // one consistent frame, and the final O / l and L = m + log l are the same
 // function -- only the rounding differs.
 //
+// Contract (the first page's flash_attention, "Build it"): Q [Nq, d],
+// K [Nk, d], V [Nk, dv] per head; O [Nq, dv]; upper-left causal masking
+// (key j visible to query i iff j <= i); no keys gives O = 0, L = -inf.
+//
 // Work split (one workgroup = 4 waves = 128 query rows of one head):
 //  * each wave owns 32 query rows; its Q block stays in registers for the
 //    whole kernel as the B operand of S^T = K Q^T (keys along M, queries
@@ -38,6 +42,8 @@
 //    (split-KV inside the workgroup, merged through LDS at the end);
 //  * causal: query block qb visits key tiles up to its diagonal only, masks
 //    are applied only on tiles that straddle the diagonal or the ragged end.
+#include <algorithm>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -50,20 +56,23 @@ constexpr int kBR = 32 * kWaves;        // query rows per workgroup
 constexpr int kComputeUnits = 256;      // MI355X
 constexpr float kRescaleSlack = 8.0f;   // log2 units: P <= 256 before a forced rescale
 
-template <int D> struct FwdTile;
-template <> struct FwdTile<128> { static constexpr int BC = 64; };
-template <> struct FwdTile<64> { static constexpr int BC = 128; };
+// keys per tile: 128 when both widths are 64, else 64 (two buffers of K and V
+// per key range fit in 64 KiB either way)
+template <int D, int DV>
+struct FwdTile {
+  static constexpr int BC = (D == 64 && DV == 64) ? 128 : 64;
+};
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // SPLIT key ranges per workgroup, each with its own double-buffered tiles
-template <int D, int SPLIT>
+template <int D, int DV, int SPLIT>
 struct FwdSmem {
-  static constexpr int BC = FwdTile<D>::BC;
+  static constexpr int BC = FwdTile<D, DV>::BC;
   bf16_raw k[SPLIT][2][BC * D];
-  bf16_raw v[SPLIT][2][BC * D];
+  bf16_raw v[SPLIT][2][BC * DV];
 };
 
 // LDS tile layout.  Each BC x D bf16 tile is stored densely, row by row,
@@ -77,9 +86,9 @@ template <int D>
 __device__ __forceinline__ constexpr int kswz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
-template <int D>
+template <int DV>
 __device__ __forceinline__ constexpr int vswz(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  return DV == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
 // Per-lane byte offsets of the 16-byte chunks one thread copies for a tile
@@ -88,22 +97,25 @@ __device__ __forceinline__ constexpr int vswz(int r) {
 // the swizzle is applied on the source side, and offsets past the end of the
 // head (the ragged last tile) read as zeros -- nothing outside the head is
 // ever read.
-template <int D>
+template <int D, int DV>
 struct TileCopy {
-  static constexpr int BC = FwdTile<D>::BC;
-  static constexpr int SLOTS = D / 8;
-  static constexpr int ROWS_PER_INSTR = 64 / SLOTS;
-  static constexpr int INSTR = BC * SLOTS / kThreads;
-  uint32_t k_off[INSTR], v_off[INSTR];
+  static constexpr int BC = FwdTile<D, DV>::BC;
+  static constexpr int KSLOTS = D / 8, VSLOTS = DV / 8;
+  static constexpr int KINSTR = BC * KSLOTS / kThreads, VINSTR = BC * VSLOTS / kThreads;
+  uint32_t k_off[KINSTR], v_off[VINSTR];
 
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < INSTR; ++i) {
-      const int blk = i * kWaves + wave;
-      const int r = blk * ROWS_PER_INSTR + lane / SLOTS;
-      const int slot = lane % SLOTS;
+    for (int i = 0; i < KINSTR; ++i) {
+      const int r = (i * kWaves + wave) * (64 / KSLOTS) + lane / KSLOTS;
+      const int slot = lane % KSLOTS;
       k_off[i] = (uint32_t)(((r & ~31) + perm32(r & 31)) * D * 2 + 16 * (slot ^ kswz<D>(r)));
-      v_off[i] = (uint32_t)(r * D * 2 + 16 * (slot ^ vswz<D>(r)));
+    }
+#pragma unroll
+    for (int i = 0; i < VINSTR; ++i) {
+      const int r = (i * kWaves + wave) * (64 / VSLOTS) + lane / VSLOTS;
+      const int slot = lane % VSLOTS;
+      v_off[i] = (uint32_t)(r * DV * 2 + 16 * (slot ^ vswz<DV>(r)));
     }
   }
 };
@@ -125,14 +137,17 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 
 // The tile offset is added to the per-lane offset, which the hardware range
 // checks against the head's size; the scalar offset stays 0.
-template <int D, bool IS_K>
-__device__ __forceinline__ void issue_tile(bf16_raw* lds_tile, __amdgpu_buffer_rsrc_t rsrc, int key0,
-                                           const TileCopy<D>& tc, int wave) {
-  const uint32_t toff = (uint32_t)key0 * D * 2;
-  const uint32_t base = lds_addr_of(lds_tile);
+template <int D, int DV>
+__device__ __forceinline__ void issue_tiles(bf16_raw* k_tile, bf16_raw* v_tile, __amdgpu_buffer_rsrc_t krs,
+                                            __amdgpu_buffer_rsrc_t vrs, int key0, const TileCopy<D, DV>& tc,
+                                            int wave) {
+  const uint32_t kbase = lds_addr_of(k_tile), vbase = lds_addr_of(v_tile);
 #pragma unroll
-  for (int i = 0; i < TileCopy<D>::INSTR; ++i)
-    lds_copy16(rsrc, (IS_K ? tc.k_off[i] : tc.v_off[i]) + toff, 0u, base + (uint32_t)(i * kWaves + wave) * 1024u);
+  for (int i = 0; i < TileCopy<D, DV>::KINSTR; ++i)
+    lds_copy16(krs, tc.k_off[i] + (uint32_t)key0 * D * 2, 0u, kbase + (uint32_t)(i * kWaves + wave) * 1024u);
+#pragma unroll
+  for (int i = 0; i < TileCopy<D, DV>::VINSTR; ++i)
+    lds_copy16(vrs, tc.v_off[i] + (uint32_t)key0 * DV * 2, 0u, vbase + (uint32_t)(i * kWaves + wave) * 1024u);
 }
 
 // S^T (BC keys x 32 queries) = K Q^T from one LDS K tile.  kaddr[kk] is the
@@ -140,11 +155,10 @@ __device__ __forceinline__ void issue_tile(bf16_raw* lds_tile, __amdgpu_buffer_r
 // block 0; key block kb adds the constant 32 * kb rows.  K operands rotate
 // through the two sets of ak (see pin()); the set used last stays live for
 // the caller to release once the scores have been consumed.
-template <int D>
-__device__ __forceinline__ void tile_scores(f32x16 (&s)[FwdTile<D>::BC / 32], const char* ktile,
-                                            const int (&kaddr)[D / 16], const bf16x8 (&qf)[D / 16],
-                                            bf16x8 (&ak)[2][FwdTile<D>::BC / 32]) {
-  constexpr int NKB = FwdTile<D>::BC / 32;
+template <int D, int BC>
+__device__ __forceinline__ void tile_scores(f32x16 (&s)[BC / 32], const char* ktile, const int (&kaddr)[D / 16],
+                                            const bf16x8 (&qf)[D / 16], bf16x8 (&ak)[2][BC / 32]) {
+  constexpr int NKB = BC / 32;
   constexpr int NKK = D / 16;
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
@@ -167,54 +181,63 @@ __device__ __forceinline__ void tile_scores(f32x16 (&s)[FwdTile<D>::BC / 32], co
 // logsumexp identity of "The identity" (FlashAttention: The Matrix You Never
 // Have to Write Down), the same merge Flash-Decoding applies across
 // workgroups ("What it doesn't solve").
-template <int D, bool CAUSAL, int SPLIT>
+//
+// Key ranges across workgroups (Flash-Decoding, "What it doesn't solve"):
+// with n_ksplit > 1 the key tiles are cut into n_ksplit contiguous ranges of
+// tiles_per_split tiles; workgroup (head, query block, range ks) writes the
+// range's own normalised output and logsumexp to O + ks * BH*Nq*DV and
+// LSE + ks * BH*Nq, and splitkv_merge_kernel combines the ranges.
+template <int D, int DV, bool CAUSAL, int SPLIT>
 __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c) {
-  constexpr int BC = FwdTile<D>::BC;
+    float* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk, int n_qblk, int n_ksplit,
+    int tiles_per_split, int total, float c) {
+  constexpr int BC = FwdTile<D, DV>::BC;
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NKK = D / 16;    // 16-wide slices of the head dimension
-  constexpr int NDB = D / 32;    // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) FwdSmem<D, SPLIT> sm;
+  constexpr int NDB = DV / 32;   // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) FwdSmem<D, DV, SPLIT> sm;
 
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
   if (blk >= total) return;
-  const int bh = blk / n_qblk;
-  int qb = blk - bh * n_qblk;
+  const int per_head = n_qblk * n_ksplit;
+  const int bh = blk / per_head;
+  const int rem = blk - bh * per_head;
+  int qb = rem / n_ksplit;
+  const int ks = rem - qb * n_ksplit;
   if (CAUSAL) qb = n_qblk - 1 - qb;  // longest rows first
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (tid >> 6) & (kWaves - 1);  // query wave: rows 32 wave .. + 31
   const int half = SPLIT == 1 ? 0 : (tid >> 8);  // key range of this wave
   const int g = lane >> 5, col = lane & 31;
-  const size_t head = (size_t)bh * N * D;
-  const bf16_raw* Qh = Q + head;
-  const bf16_raw* Kh = K + head;
-  const bf16_raw* Vh = V + head;
+  const bf16_raw* Qh = Q + (size_t)bh * Nq * D;
+  const bf16_raw* Kh = K + (size_t)bh * Nk * D;
+  const bf16_raw* Vh = V + (size_t)bh * Nk * DV;
 
   const int q_start = qb * kBR;
   const int q0w = q_start + 32 * wave;
   const int my_q = q0w + col;
 
-  const int kv_end = CAUSAL ? min(N, q_start + kBR) : N;
-  const int n_tiles = (kv_end + BC - 1) / BC;
-  // tiles [t_first, t_end) of this wave's key range; every wave runs n_iter
+  // key tiles [ks_first, ks_end) of this workgroup: its key range, cut at
+  // the causal diagonal of the query block
+  const int kv_end = CAUSAL ? min(Nk, q_start + kBR) : Nk;
+  const int ks_first = ks * tiles_per_split;
+  const int ks_end = min((kv_end + BC - 1) / BC, ks_first + tiles_per_split);
+  const int n_tiles = max(ks_end - ks_first, 0);
+  // tiles [t_first, t_end) of this wave's half of it; every wave runs n_iter
   // iterations so that the workgroup barriers line up
   const int n_iter = (n_tiles + SPLIT - 1) / SPLIT;
-  const int t_first = half * n_iter;
-  const int t_end = min(n_tiles, t_first + n_iter);
+  const int t_first = ks_first + half * n_iter;
+  const int t_end = min(ks_first + n_tiles, t_first + n_iter);
 
-  TileCopy<D> tc;
+  TileCopy<D, DV> tc;
   tc.init(wave, lane);
   // per-head buffer descriptors: reads past the head's last key return 0
-  const int head_bytes = N * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, head_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, Nk * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, Nk * DV * 2, 0x00020000);
   // prologue loads: first K and V tile of the range
-  if (t_first < t_end) {
-    issue_tile<D, true>(sm.k[half][0], krs, t_first * BC, tc, wave);
-    issue_tile<D, false>(sm.v[half][0], vrs, t_first * BC, tc, wave);
-  }
+  if (t_first < t_end) issue_tiles<D, DV>(sm.k[half][0], sm.v[half][0], krs, vrs, t_first * BC, tc, wave);
 
   // loop-invariant lane parts of the LDS operand addresses (bytes)
   int kaddr[NKK];
@@ -226,12 +249,12 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   for (int db = 0; db < NDB; ++db) {
     const int kr = 8 * (grp >> 1) + (sl >> 2);  // row within a 16-row slice (plus constants)
     const int d = 32 * db + 16 * (grp & 1) + 4 * (sl & 3);
-    vaddr[db] = kr * D * 2 + 16 * ((d >> 3) ^ vswz<D>(kr)) + 2 * (d & 7);
+    vaddr[db] = kr * DV * 2 + 16 * ((d >> 3) ^ vswz<DV>(kr)) + 2 * (d & 7);
   }
 
   bf16x8 qf[NKK];
   {
-    const int qr = min(my_q, N - 1);
+    const int qr = min(my_q, Nq - 1);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(ld16(Qh + (size_t)qr * D + 16 * kk + 8 * g));
   }
@@ -265,20 +288,22 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
     wait_tile_loads();
     __syncthreads();
     if (t >= t_end) continue;  // the shorter key range idles through the barriers
-    if (t + 1 < t_end) {
-      issue_tile<D, true>(sm.k[half][(it + 1) & 1], krs, key0 + BC, tc, wave);
-      issue_tile<D, false>(sm.v[half][(it + 1) & 1], vrs, key0 + BC, tc, wave);
-    }
-    tile_scores<D>(s_cur, reinterpret_cast<const char*>(sm.k[half][it & 1]), kaddr, qf, ak);
+    if (t + 1 < t_end)
+      issue_tiles<D, DV>(sm.k[half][(it + 1) & 1], sm.v[half][(it + 1) & 1], krs, vrs, key0 + BC, tc, wave);
+    tile_scores<D, BC>(s_cur, reinterpret_cast<const char*>(sm.k[half][it & 1]), kaddr, qf, ak);
 
-    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > N;
+    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > Nk;
     if (need_mask) {
+      // register 8 h + e of half g holds key key0 + 32 kb + 16 h + 8 g + e;
+      // keys above last_key (causal: the row; always: Nk - 1) are masked
+      const int last_key = CAUSAL ? min(my_q, Nk - 1) : Nk - 1;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + 32 * kb + perm_row(i, g);
-          if (key >= N || (CAUSAL && key > my_q)) s_cur[kb][i] = -INFINITY;
+        for (int h = 0; h < 2; ++h) {
+          const int lim = last_key - (key0 + 32 * kb + 16 * h + 8 * g);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s_cur[kb][8 * h + e] = e > lim ? -INFINITY : s_cur[kb][8 * h + e];
         }
     }
     // tile row max (both lane halves), in log2 units
@@ -348,7 +373,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
 #pragma unroll
           for (int rr = 0; rr < 2; ++rr)
             part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16*)(vtile + vaddr[db] + (32 * kb + 16 * h + 4 * rr) * D * 2));
+                (lds_v4i16*)(vtile + vaddr[db] + (32 * kb + 16 * h + 4 * rr) * DV * 2));
           a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
@@ -392,11 +417,12 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   }
 
   // epilogue: combine the two half-row sums, normalise once, write O and L
+  // (of this workgroup's key range when the keys are split across workgroups)
   const float l_tot = halves_sum(l_run);
   const float l_nrm = halves_sum(l_rnd);
-  if (my_q < N) {
+  if (my_q < Nq) {
     const float inv = l_nrm > 0.f ? 1.f / l_nrm : 0.f;
-    float* Orow = O + head + (size_t)my_q * D;
+    float* Orow = O + ((size_t)ks * BH + bh) * Nq * DV + (size_t)my_q * DV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -408,40 +434,115 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
         v.w = oacc[db][4 * i4 + 3] * inv;
         *reinterpret_cast<float4*>(Orow + 32 * db + 8 * i4 + 4 * g) = v;
       }
-    if (g == 0) LSE[(size_t)bh * N + my_q] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (g == 0) LSE[((size_t)ks * BH + bh) * Nq + my_q] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int N,
-                  float scale, hipStream_t stream) {
-  const int n_qblk = (N + kBR - 1) / kBR;
-  const long long total = (long long)BH * n_qblk;
+// Merges n_split partial (O_s, L_s) of each query row (written by the
+// forward with key ranges across workgroups) with the logsumexp identity:
+// L = m + ln sum_s e^(L_s - m), O = sum_s e^(L_s - L) O_s; rows whose
+// ranges all saw no key get O = 0, L = -inf.  One thread per 4 columns.
+template <int DV>
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ Opart,
+                                                            const float* __restrict__ Lpart, float* __restrict__ O,
+                                                            float* __restrict__ LSE, long long rows, int n_split) {
+  constexpr int TPR = DV / 4;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid / TPR;
+  const int part = (int)(gid % TPR);
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, Lpart[(size_t)sp * rows + row]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  if (m != -INFINITY) {
+    for (int sp = 0; sp < n_split; ++sp) {
+      const float w = __expf(Lpart[(size_t)sp * rows + row] - m);
+      const float4 o = *reinterpret_cast<const float4*>(Opart + ((size_t)sp * rows + row) * DV + 4 * part);
+      acc.x += w * o.x;
+      acc.y += w * o.y;
+      acc.z += w * o.z;
+      acc.w += w * o.w;
+      den += w;
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  *reinterpret_cast<float4*>(O + (size_t)row * DV + 4 * part) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (part == 0) LSE[row] = den > 0.f ? m + __logf(den) : -INFINITY;
+}
+
+template <int D, int DV, bool CAUSAL>
+hipError_t launch(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
+                  int n_ksplit, float* ws, float scale, hipStream_t stream) {
+  constexpr int BC = FwdTile<D, DV>::BC;
+  const int n_qblk = (Nq + kBR - 1) / kBR;
+  const int n_ktiles = (Nk + BC - 1) / BC;
+  n_ksplit = max(1, min(n_ksplit, max(n_ktiles, 1)));
+  const int tiles_per_split = n_ktiles == 0 ? 1 : (n_ktiles + n_ksplit - 1) / n_ksplit;
+  n_ksplit = n_ktiles == 0 ? 1 : (n_ktiles + tiles_per_split - 1) / tiles_per_split;
+  const long long total = (long long)BH * n_qblk * n_ksplit;
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
+  float* o_dst = n_ksplit > 1 ? ws : o;
+  float* l_dst = n_ksplit > 1 ? ws + (size_t)n_ksplit * BH * Nq * DV : lse;
   // Two 4-wave workgroups per CU keep two waves on every SIMD; a grid too
-  // small for that (fewer than two workgroups per CU) splits each query
-  // block's keys over 8 waves instead.
-  const bool split = total < 2 * kComputeUnits && N > FwdTile<D>::BC;
+  // small for that (fewer than two workgroups per CU) splits each
+  // workgroup's key tiles over 8 waves instead.
+  const bool split = total < 2 * kComputeUnits && (n_ktiles + n_ksplit - 1) / n_ksplit > 1;
   if (split)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2>), dim3(grid), dim3(2 * kThreads), 0, stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 2>), dim3(grid), dim3(2 * kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
-                       static_cast<const bf16_raw*>(v), o, lse, N, n_qblk, (int)total, scale * kLog2e);
+                       static_cast<const bf16_raw*>(v), o_dst, l_dst, BH, Nq, Nk, n_qblk, n_ksplit, tiles_per_split,
+                       (int)total, scale * kLog2e);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 1>), dim3(grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 1>), dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
-                       static_cast<const bf16_raw*>(v), o, lse, N, n_qblk, (int)total, scale * kLog2e);
+                       static_cast<const bf16_raw*>(v), o_dst, l_dst, BH, Nq, Nk, n_qblk, n_ksplit, tiles_per_split,
+                       (int)total, scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_ksplit == 1) return e;
+  const long long rows = (long long)BH * Nq;
+  const long long threads = rows * (DV / 4);
+  const long long mgrid = (threads + 255) / 256;
+  if (mgrid > (1LL << 31) - 1) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((splitkv_merge_kernel<DV>), dim3((unsigned)mgrid), dim3(256), 0, stream, o_dst, l_dst, o, lse,
+                     rows, n_ksplit);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dv(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
+                     int dv, int n_ksplit, float* ws, float scale, hipStream_t stream) {
+  return dv == 128 ? launch<D, 128, CAUSAL>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, stream)
+                   : launch<D, 64, CAUSAL>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int N,
-                           int d, float scale, int causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch<128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                              : launch<128, false>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch<64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch<64, false>(q, k, v, o, lse, BH, N, scale, stream);
+int fwd_splitkv_resolve(int BH, int Nq, int Nk, int d, int dv, int n_splits) {
+  const int BC = (d == 64 && dv == 64) ? 128 : 64;
+  const int n_ktiles = (Nk + BC - 1) / BC;
+  if (n_ktiles <= 1) return 1;
+  if (n_splits <= 0) {
+    // enough workgroups for two per CU, and each range at least 4 tiles
+    const long long base = (long long)BH * ((Nq + kBR - 1) / kBR);
+    long long want = (2LL * kComputeUnits + base - 1) / base;
+    want = std::min<long long>(want, std::max(1, n_ktiles / 4));
+    n_splits = (int)std::max<long long>(1, std::min<long long>(want, 256));
+  }
+  n_splits = std::min(n_splits, n_ktiles);
+  const int tps = (n_ktiles + n_splits - 1) / n_splits;
+  return (n_ktiles + tps - 1) / tps;
+}
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq,
+                           int Nk, int d, int dv, int causal, int n_ksplit, float* ws, float scale,
+                           hipStream_t stream) {
+  if (d == 128) return causal ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, stream)
+                              : launch_dv<128, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, stream);
+  return causal ? launch_dv<64, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, stream)
+                : launch_dv<64, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, stream);
 }
 
 }  // namespace fa

@@ -7,8 +7,16 @@
 
 namespace fa {
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int N,
-                           int d, float scale, int causal, hipStream_t stream);
+// Forward, bf16 inputs: Q [BH, Nq, d], K [BH, Nk, d], V [BH, Nk, dv].
+// n_ksplit > 1 cuts the key tiles into that many ranges processed by separate
+// workgroups; ws then holds n_ksplit * BH * Nq * (dv + 1) floats of partial
+// results (fwd_splitkv_resolve gives the count actually used).
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq,
+                           int Nk, int d, int dv, int causal, int n_ksplit, float* ws, float scale,
+                           hipStream_t stream);
+// Number of key ranges a split-KV forward uses for n_splits requested
+// (0: chosen for the grid); 1 means no split and no workspace.
+int fwd_splitkv_resolve(int BH, int Nq, int Nk, int d, int dv, int n_splits);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N,
                           int d, float scale, int causal, hipStream_t stream);

@@ -89,6 +89,15 @@ def make_inputs(w: Workload, with_do=None):
     return out
 
 
+def make_general(B, H, Nq, Nk, d, dv, seed, std=1.0):
+    """Seeded bf16 Q [B,H,Nq,d], K [B,H,Nk,d], V [B,H,Nk,dv] (CPU tensors) for
+    the general forward contract; seeds 1000*seed + {q:1, k:2, v:3}."""
+    base = 1000 * int(seed)
+    return {"q": draw((B, H, Nq, d), base + _TENSOR_SEED["q"], std),
+            "k": draw((B, H, Nk, d), base + _TENSOR_SEED["k"], std),
+            "v": draw((B, H, Nk, dv), base + _TENSOR_SEED["v"])}
+
+
 def sample_rows(N, count, seed):
     """Rows 0 and N-1 plus ``count - 2`` distinct other rows, sorted."""
     if count >= N:

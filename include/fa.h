@@ -53,7 +53,7 @@ typedef enum {
                            float32 tensor must be byte-addressable in 31 bits) */
   FA_ERR_HEADDIM = 3,   /* d is not a supported head width (64 or 128)         */
   FA_ERR_SCALE = 4,     /* scale is not finite and > 0                         */
-  FA_ERR_WORKSPACE = 5, /* backward workspace missing                          */
+  FA_ERR_WORKSPACE = 5, /* a required workspace is NULL                        */
   FA_ERR_HIP = 6        /* a kernel launch was rejected by the HIP runtime     */
 } fa_status;
 
@@ -71,6 +71,39 @@ typedef enum {
  */
 int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * General forward, the first page's flash_attention contract ("Build it"):
+ *   q : device, bf16 [B,H,Nq,d]      k : device, bf16 [B,H,Nk,d]
+ *   v : device, bf16 [B,H,Nk,dv]     o : device, float32 [B,H,Nq,dv]
+ *   lse : device, float32 [B,H,Nq]
+ *   d, dv : 64 or 128 each.  Nq and Nk are independent; causal masking is
+ *   upper-left for any Nq, Nk (key j visible to query i iff j <= i).
+ *   Nk == 0 (no keys) gives o = 0 and lse = -inf for every row, per the
+ *   page's empty-key policy ("Check it"); q, k, v may then be NULL.
+ * fa_fwd(q,k,v,o,lse,B,H,N,d,...) is fa_fwd_ex(...,Nq=N,Nk=N,d,dv=d,...).
+ * Per head, Nq*dv*4, Nk*d*2 and Nk*dv*2 bytes must stay below 2^31.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,
+              int B, int H, int Nq, int Nk, int d, int dv, float scale, int causal, hipStream_t stream);
+
+/*
+ * Split-KV forward (Flash-Decoding, "What it doesn't solve" on the first
+ * page): for few query rows and long key sequences, the key tiles are cut
+ * into contiguous ranges that separate workgroups process in parallel; each
+ * writes a partial (O, L) into `workspace`, and a second kernel merges them
+ * with the logsumexp identity ("The identity").  Same contract and results
+ * (up to rounding) as fa_fwd_ex.
+ *   n_splits : 1 .. 256 ranges requested (capped at the number of key
+ *              tiles), or 0 to let the library choose for the grid.
+ *   workspace: device, >= fa_fwd_splitkv_workspace_bytes(...) bytes for the
+ *              same arguments (0 bytes -- and NULL allowed -- when the
+ *              request resolves to a single range).
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dv, int n_splits);
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float* lse, void* workspace,
+                   int B, int H, int Nq, int Nk, int d, int dv, float scale, int causal, int n_splits,
+                   hipStream_t stream);
 
 /*
  * Forward pass with float32 inputs, computed entirely in float32 (same

@@ -112,6 +112,66 @@ def test_fwd_split_and_single_range_paths_agree(d, causal):
     assert np.array_equal(o_big[:, :2], o_big[:, 2:4])  # identical heads, identical results
 
 
+# ------------------------------------------------------------------ the page's general contract (fa_fwd_ex)
+GENERAL_SHAPES = [(1, 1000), (37, 300), (300, 37), (129, 129), (1000, 100), (64, 4097)]
+
+
+@pytest.mark.parametrize("d,dv", [(64, 128), (128, 64), (128, 128), (64, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", GENERAL_SHAPES)
+def test_fwd_general_shapes(nq, nk, d, dv, causal):
+    # Nq != Nk with upper-left causal masking, dv != d ("Build it")
+    t = I.make_general(1, 2, nq, nk, d, dv, 800 + nq + nk + d + dv)
+    say(f"fwd general Nq={nq} Nk={nk} d={d} dv={dv} causal={causal}")
+    o, l = run_fwd(t, causal)
+    assert o.shape == (1, 2, nq, dv) and l.shape == (1, 2, nq)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(d))
+    check_fwd(o, l, oref, lref, f"general Nq={nq} Nk={nk} d={d} dv={dv} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_no_keys_gives_zero_and_minus_inf(causal):
+    # the page's empty-key policy ("Check it"): O = 0, L = -inf
+    t = I.make_general(2, 3, 50, 0, 128, 64, 901)
+    q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
+    o = torch.full((2, 3, 50, 64), 7.0, device="cuda")
+    l = torch.full((2, 3, 50), 7.0, device="cuda")
+    fa.forward(q, k, v, causal=causal, out=o, lse=l)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+    o2, l2 = fa.forward_splitkv(q, k, v, causal=causal, n_splits=4)
+    torch.cuda.synchronize()
+    assert torch.all(o2 == 0) and torch.all(torch.isneginf(l2))
+
+
+# ------------------------------------------------------------------ split-KV across workgroups (fa_fwd_splitkv)
+@pytest.mark.parametrize("d,dv", [(128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk,splits", [(1, 4097, 0), (1, 4097, 3), (4, 8192, 16), (200, 3000, 5), (1, 64, 4)])
+def test_fwd_splitkv(nq, nk, splits, d, dv, causal):
+    t = I.make_general(2, 2, nq, nk, d, dv, 1000 + nq + nk + splits + d)
+    say(f"fwd splitkv Nq={nq} Nk={nk} splits={splits} d={d} dv={dv} causal={causal}")
+    q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
+    o, l = fa.forward_splitkv(q, k, v, causal=causal, n_splits=splits)
+    o1, l1 = fa.forward(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(d))
+    check_fwd(o.cpu().numpy(), l.cpu().numpy(), oref, lref, f"splitkv Nq={nq} Nk={nk} splits={splits}")
+    # the merged ranges agree with the single-range kernel to rounding
+    assert float((o - o1).abs().max()) <= 5e-3 and float((l - l1).abs().max()) <= 5e-4
+
+
+def test_fwd_splitkv_decode_long_context():
+    # decoding: one query row per head against 32768 keys, 32 heads
+    t = I.make_general(1, 32, 1, 32768, 128, 128, 1100)
+    say("fwd splitkv decode B1 H32 Nq1 Nk32768 d128")
+    q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
+    o, l = fa.forward_splitkv(q, k, v)
+    torch.cuda.synchronize()
+    oref, lref = oracle_fwd(t, False, 1 / math.sqrt(128))
+    check_fwd(o.cpu().numpy(), l.cpu().numpy(), oref, lref, "decode 32k")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 37, 129, 300])
