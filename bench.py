@@ -10,6 +10,8 @@ the step: 3.5 * (4*B*H*N^2*d / 2) FLOP per step (forward counted as
 
 Also reported on the same line:
   fwd        forward alone on B=1, H=8, N=4096, d=128, non-causal
+  decode     split-KV forward (fa_fwd_splitkv), one query row per head against
+             32768 keys, B=1, H=32, d=dv=128, against the HBM roofline
   phases     forward and backward of the step timed separately
   kernels    each kernel of the step timed alone through its C entry point
              (fa_fwd, fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq)
@@ -33,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2048 bf16 FMA/clk (4096 FLOP) x 2.4 GHz, dense
+HBM_PEAK_GBS = 8000.0      # HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -197,6 +200,26 @@ def main():
     f2 = wf.fwd_flop() / (ms_f2 * 1e-3) / 1e12
     f2_traffic, f2_src = committed_traffic("fwd_d128_split2")
 
+    # ------------------------------------------------------------ decode (split-KV across workgroups)
+    dc = I.DECODE_32K
+    td = I.make_general(dc["B"], dc["H"], dc["Nq"], dc["Nk"], dc["d"], dc["dv"], dc["seed"])
+    qd, kd, vd = (td[n].to(dev) for n in ("q", "k", "v"))
+    od = torch.empty((dc["B"], dc["H"], dc["Nq"], dc["dv"]), dtype=torch.float32, device=dev)
+    ld = torch.empty((dc["B"], dc["H"], dc["Nq"]), dtype=torch.float32, device=dev)
+    wsd = torch.empty((max(4, fa.library().fa_fwd_splitkv_workspace_bytes(
+        dc["B"], dc["H"], dc["Nq"], dc["Nk"], dc["d"], dc["dv"], 0)),), dtype=torch.uint8, device=dev)
+
+    def dec():
+        fa.forward_splitkv(qd, kd, vd, workspace=wsd, out=od, lse=ld)
+
+    for _ in range(args.warmup):
+        dec()
+    ms_dec = time_calls(dec, args.steps, stream)
+    bh = dc["B"] * dc["H"]
+    dec_bytes = (bh * dc["Nq"] * dc["d"] * 2 + bh * dc["Nk"] * (dc["d"] + dc["dv"]) * 2
+                 + bh * dc["Nq"] * (dc["dv"] + 1) * 4)
+    dec_gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
+
     res = {
         "metric": "attention TFLOP/s (fwd, fwd+bwd) bf16 at 1 MI355X; % of MFMA peak",
         "value": round(value, 2),
@@ -250,6 +273,20 @@ def main():
                 "traffic": f2_traffic,
                 "traffic_source": f2_src,
                 "algorithmic_flop_per_launch": wf.fwd_flop(),
+            },
+        },
+        "decode": {
+            "workload": dc["name"],
+            "ms": round(ms_dec, 4),
+            "roofline": {
+                "kernel": "fwd_bf16_kernel, key ranges across workgroups, + splitkv_merge_kernel (the fa_fwd_splitkv call)",
+                "bound": "hbm",
+                "achieved": round(dec_gbs, 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "algorithmic_bytes_per_call": dec_bytes,
             },
         },
         "timed_wall_s": round(wall, 3),

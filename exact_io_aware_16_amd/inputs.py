@@ -98,6 +98,11 @@ def make_general(B, H, Nq, Nk, d, dv, seed, std=1.0):
             "v": draw((B, H, Nk, dv), base + _TENSOR_SEED["v"])}
 
 
+# Decoding: one query row per head against a long key sequence (split-KV).
+DECODE_32K = {"name": "decode_bf16_b1h32nq1nk32768d128", "B": 1, "H": 32, "Nq": 1, "Nk": 32768, "d": 128,
+              "dv": 128, "seed": 6}
+
+
 def sample_rows(N, count, seed):
     """Rows 0 and N-1 plus ``count - 2`` distinct other rows, sorted."""
     if count >= N:
