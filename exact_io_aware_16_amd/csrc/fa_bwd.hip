@@ -41,6 +41,8 @@
 //  the transpose reads of a tile without LDS bank conflicts; every per-lane
 //  LDS address is a lane constant XOR a compile-time mask, plus an
 //  immediate.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 #include "fa_lds.h"
@@ -85,13 +87,20 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBKV = 32 * kWaves;  // keys per workgroup
 constexpr int kBQ = 64;            // query rows per step
+// operand loads run kAhead MFMA groups ahead, through kSets register sets
+constexpr int kAhead = 3;
+constexpr int kSets = kAhead + 1;
+
+// three query tiles in flight: step st's (dV / dK products), step st+1's
+// (S / dP products) and step st+2's (arriving)
+constexpr int kTiles = 3;
 
 template <int D>
 struct DkdvSmem {
-  bf16_raw q[2][kBQ * D];        // Q tiles, rows in perm32 order
-  bf16_raw dout[2][kBQ * D];     // dO tiles, rows in perm32 order
-  float l2[2][kBQ];              // L log2(e) of the tile's rows
-  float dsc[2][kBQ];             // scale * D of the tile's rows
+  bf16_raw q[kTiles][kBQ * D];     // Q tiles, rows in perm32 order
+  bf16_raw dout[kTiles][kBQ * D];  // dO tiles, rows in perm32 order
+  float l2[kTiles][kBQ];           // L log2(e) of the tile's rows
+  float dsc[kTiles][kBQ];          // scale * D of the tile's rows
 };
 
 // 16-byte chunks a thread copies for one BQ x D query tile: LDS block
@@ -122,8 +131,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   constexpr int NDB = D / 32;  // 32-row blocks of dK^T / dV^T
   constexpr int RB = D * 2;    // bytes per Q / dO / K row
   constexpr uint32_t kTileBytes = kBQ * D * 2;
-  constexpr uint32_t kDoutMinusQ = 2 * kTileBytes;  // sm.dout[b] - sm.q[b]
-  constexpr uint32_t kDscMinusL2 = 2 * kBQ * 4;     // sm.dsc[b] - sm.l2[b]
+  constexpr uint32_t kDoutMinusQ = kTiles * kTileBytes;  // sm.dout[b] - sm.q[b]
+  constexpr uint32_t kDscMinusL2 = kTiles * kBQ * 4;     // sm.dsc[b] - sm.l2[b]
   __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
 
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -197,19 +206,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       dv_acc[db][i] = 0.f;
     }
 
-  // Operand register sets (see pin()).  Each MFMA phase keeps three sets and
-  // loads group g + 2 while group g runs: the set it overwrites was last
-  // read by group g - 1, which has started once group g is issued.
-  //   ar: Q / dO rows of the S and dP products (one query block, k-slice)
-  //   at: dO^T / Q^T transpose reads of the dV and dK products
-  //   pb, dsb: P and dS' tiles (B operands)
-  constexpr int NCG = 4 * NDB;  // (query block, half, head-dim block) groups of phase C
-  constexpr int NAG = 2 * NKK;   // (k-slice, query block) groups of phase A
-  bf16x8 ar[3][2], at[3][2], pb[2][2], dsb[2][2];
+  // ---- software pipeline over steps.  Step st's work is four MFMA phases
+  // of G groups (two MFMAs each):
+  //   A0 / A1: S and dP of query block 0 / 1 (32 rows) against the wave's keys
+  //   C0 / C1: dV^T, dK^T from query block 0 / 1
+  // and the softmax of each block (P, dS') on the vector ALUs.  Iteration st
+  // runs   A0(st+1) | C0(st) | A1(st+1) | C1(st)
+  // with softmax(st, block 1) spread over the groups of the first two phases
+  // and softmax(st+1, block 0) over the last two, so every matrix-core phase
+  // has independent vector work beside it.  The prologue runs A0(0), A1(0) and
+  // softmax(0, block 0); the last step runs C0, C1 with softmax(block 1).
+  constexpr int G = NKK;  // groups per phase (= 2 NDB)
+  // Operand ring (see pin()): every group takes two operands -- Q and dO rows
+  // in phases A, dO^T and Q^T transpose reads in phases C.  Group g + kAhead
+  // loads into set (g + kAhead) % kSets while group g runs: that set was last
+  // read by group g - 1, which has started once group g is issued.  Group
+  // counts per run (4G, 2G) are multiples of kSets, so the sets a run loads
+  // first were not read by the previous run's last group.
+  static_assert((2 * G) % kSets == 0, "operand ring must restart on a phase boundary");
+  bf16x8 op[kSets][2], pb[2][2], dsb[2][2];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) ar[j][0] = ar[j][1] = at[j][0] = at[j][1] = bf16x8{};
+  for (int j = 0; j < kSets; ++j) op[j][0] = op[j][1] = bf16x8{};
 #pragma unroll
   for (int j = 0; j < 2; ++j) pb[j][0] = pb[j][1] = dsb[j][0] = dsb[j][1] = bf16x8{};
+  f32x16 s[2], dp[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) s[j] = dp[j] = f32x16{};
 
   // ---- per-lane LDS address constants.  Every tile base is a multiple of
   // 1 KiB, so XOR masks below bit 10 pass through the base.
@@ -226,152 +248,195 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const uint32_t q_base0 = lds_addr_of(sm.q[0]);
   const uint32_t l2_base0 = lds_addr_of(sm.l2[0]);
 
+  // per-step context: LDS addresses in the step's tile buffer, first query
+  // row, whether the step's pairs need masking
+  struct Step {
+    uint32_t qrow, tq, tq1, l2;
+    int q0;
+    bool mask;
+  };
+  auto step_ctx = [&](int st) {
+    const uint32_t b = (uint32_t)(st % kTiles);
+    const uint32_t qbase = q_base0 + b * kTileBytes;
+    Step x;
+    x.qrow = opaque(qbase + row_lane);
+    x.tq = opaque(qbase + tq_lane);
+    x.tq1 = opaque(x.tq ^ 32u);  // row + 8: swizzle ^ 2
+    x.l2 = l2_base0 + b * (kBQ * 4) + (uint32_t)(32 * g);
+    x.q0 = q_first + st * kBQ;
+    x.mask = (CAUSAL && x.q0 < k0 + kBKV) || k0 + kBKV > N;
+    return x;
+  };
+
+  // phase A group (query block qb, k-slice kk) and phase C group (qh = 2 qb + h,
+  // head-dim block db): operand loads and products
+  auto load_a = [&](const Step& x, int qb, int kk, bf16x8(&o)[2]) {
+    const uint32_t ra = (x.qrow ^ (uint32_t)(32 * kk)) + (uint32_t)(32 * qb * RB);
+    o[0] = lds_row16(ra);
+    o[1] = lds_row16(ra + kDoutMinusQ);
+  };
+  auto load_c = [&](const Step& x, int qh, int db, bf16x8(&o)[2]) {
+    const uint32_t rows = (uint32_t)(16 * qh * RB);
+    const uint32_t o0 = (x.tq ^ (uint32_t)(64 * db)) + rows;
+    const uint32_t o1 = (x.tq1 ^ (uint32_t)(64 * db)) + rows + 8 * RB;
+    o[0] = tr_pair(o0 + kDoutMinusQ, o1 + kDoutMinusQ);
+    o[1] = tr_pair(o0, o1);
+  };
+  auto mfma_a = [&](int qb, int kk, const bf16x8(&o)[2]) {
+    s[qb] = mfma32(o[0], kres[kk], kk == 0 ? f32x16{} : s[qb]);
+    dp[qb] = mfma32(o[1], vres[kk], kk == 0 ? f32x16{} : dp[qb]);
+    anchor_a(s[qb]);
+    anchor_a(dp[qb]);
+  };
+  auto mfma_c = [&](int qh, int db, const bf16x8(&o)[2]) {
+    dv_acc[db] = mfma32(o[0], pb[qh >> 1][qh & 1], dv_acc[db]);
+    dk_acc[db] = mfma32(o[1], dsb[qh >> 1][qh & 1], dk_acc[db]);
+    anchor_a(dv_acc[db]);
+    anchor_a(dk_acc[db]);
+  };
+
+  // ---- softmax of query block qb of a step in 8 pieces of 2 elements per
+  // lane: P = exp2(S c - L log2 e), dS' = P (scale dP - scale D); masked
+  // pairs get 0.  Chunk h = piece / 4 covers 8 consecutive query rows.
+  float lv[8], dd[8], pv[8], dv8[8];
+  int dead = 0;
+  auto softmax_piece = [&](const Step& x, int qb, int piece) {
+    const int h = piece >> 2, e0 = 2 * (piece & 3);
+    const uint32_t qr = (uint32_t)(32 * qb + 16 * h);  // + 8 g: 8 consecutive local query rows
+    if ((piece & 3) == 0) {
+      const f32x4 l0 = *(lds_f4*)(uintptr_t)(x.l2 + 4 * qr);
+      const f32x4 l1 = *(lds_f4*)(uintptr_t)(x.l2 + 4 * qr + 16);
+      const f32x4 d0 = *(lds_f4*)(uintptr_t)(x.l2 + kDscMinusL2 + 4 * qr);
+      const f32x4 d1 = *(lds_f4*)(uintptr_t)(x.l2 + kDscMinusL2 + 4 * qr + 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lv[e] = l0[e];
+        lv[4 + e] = l1[e];
+        dd[e] = d0[e];
+        dd[4 + e] = d1[e];
+      }
+      // masked pairs of this chunk: e < dead (row q0 + qr + 8 g + e sees
+      // key my_key iff my_key <= that row, and only keys below N exist)
+      if (x.mask) {
+        dead = CAUSAL ? my_key - (x.q0 + (int)qr + 8 * g) : 0;
+        dead = my_key >= N ? 8 : dead;
+      }
+    }
+#pragma unroll
+    for (int e = e0; e < e0 + 2; ++e) {
+      float pe = fast_exp2(fmaf(s[qb][8 * h + e], c, -lv[e]));
+      if (x.mask) pe = e < dead ? 0.f : pe;
+      pv[e] = pe;
+      dv8[e] = pe * fmaf(dp[qb][8 * h + e], scale, -dd[e]);
+    }
+    if ((piece & 3) == 3) {
+      pb[qb][h] = pack_bf16x8(pv);
+      dsb[qb][h] = pack_bf16x8(dv8);
+    }
+  };
+
+  // ---- one run of NG groups.  group(gi, ld, mm, o) loads group gi's
+  // operands into o (ld) or issues its products from o (mm); between(gi)
+  // runs vector work after group gi has issued.  At gi = 0 the ring pin
+  // keeps the set read by the previous run's last group alive past the
+  // run's first product, so no preamble load reuses its registers.
+  auto run = [&](auto n_groups, auto group, auto between) {
+    constexpr int NG = decltype(n_groups)::value;
+#pragma unroll
+    for (int gi = 0; gi < kAhead; ++gi) group(gi, true, false, op[gi % kSets]);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      group(gi, false, true, op[gi % kSets]);
+      group_fence();
+      pin(op[(gi + kAhead) % kSets][0]);
+      pin(op[(gi + kAhead) % kSets][1]);
+      if (gi + kAhead < NG) group(gi + kAhead, true, false, op[(gi + kAhead) % kSets]);
+      between(gi);
+    }
+  };
+  using G2 = std::integral_constant<int, 2 * G>;
+  using G4 = std::integral_constant<int, 4 * G>;
+
+  // ---- prologue: A0(0), A1(0) with softmax(0, block 0) beside A1
   wait_loads();
-  for (int st = 0; st < n_steps; ++st) {
-    const int q0 = q_first + st * kBQ;
-    const uint32_t buf = (uint32_t)(st & 1);
-    __syncthreads();  // tile st visible; every wave is done with tile st-1
-    if (st + 1 < n_steps) issue_qtile(buf ^ 1u, q0 + kBQ);
-    const uint32_t qbase = q_base0 + buf * kTileBytes;
+  __syncthreads();  // tile 0 visible
+  if (n_steps > 1) issue_qtile(1u, q_first + kBQ);
+  {
+    const Step x0 = step_ctx(0);
+    run(G2{},
+        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
+          const int qb = gi / G, kk = gi % G;
+          if (ld) load_a(x0, qb, kk, o);
+          if (mm) mfma_a(qb, kk, o);
+        },
+        [&](int gi) {
+          if (gi >= G)
+#pragma unroll
+            for (int pc = (8 * (gi - G)) / G; pc < (8 * (gi - G + 1)) / G; ++pc) softmax_piece(x0, 0, pc);
+        });
+  }
+  wait_loads();  // this wave's copies of tile 1 have landed
 
-    // The step runs as four MFMA phases; the softmax of one query block
-    // runs on the vector ALUs between the MFMA groups of the next phase:
-    //   A0: S, dP of query block 0      A1: S, dP of block 1  + softmax(0)
-    //   C0: dV, dK from block 0 + softmax(1)      C1: dV, dK from block 1
-    f32x16 s[2], dp[2];
-    const uint32_t qrow = opaque(qbase + row_lane);
-    // phase-A group ga = NKK qb + kk: Q and dO rows of block qb, k-slice kk
-    auto load_a = [&](int ga) {
-      const int qb = ga / NKK, kk = ga % NKK;
-      const uint32_t ra = (qrow ^ (uint32_t)(32 * kk)) + (uint32_t)(32 * qb * RB);
-      ar[ga % 3][0] = lds_row16(ra);
-      ar[ga % 3][1] = lds_row16(ra + kDoutMinusQ);
-    };
-    const uint32_t tq = opaque(qbase + tq_lane);
-    const uint32_t tq1 = opaque(tq ^ 32u);  // row + 8: swizzle ^ 2
-    // phase-C group gi = NDB (2 qb + h) + db
-    auto load_c = [&](int gi) {
-      const int qh = gi / NDB, db = gi % NDB;  // qh = 2 qb + h
-      bf16x8(&a)[2] = at[gi % 3];
-      const uint32_t rows = (uint32_t)(16 * qh * RB);
-      const uint32_t o0 = (tq ^ (uint32_t)(64 * db)) + rows;
-      const uint32_t o1 = (tq1 ^ (uint32_t)(64 * db)) + rows + 8 * RB;
-      a[0] = tr_pair(o0 + kDoutMinusQ, o1 + kDoutMinusQ);
-      a[1] = tr_pair(o0, o1);
-    };
+  // ---- steady state: A0(st+1) | C0(st) | A1(st+1) | C1(st)
+  for (int st = 0; st + 1 < n_steps; ++st) {
+    __syncthreads();  // tile st+1 visible; every wave is done with tile st-1
+    if (st + 2 < n_steps) issue_qtile((uint32_t)((st + 2) % kTiles), q_first + (st + 2) * kBQ);
+    const Step xc = step_ctx(st), xn = step_ctx(st + 1);
+    run(G4{},
+        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
+          const int ph = gi / G, i = gi % G;
+          if (ph == 0 || ph == 2) {  // A0, A1 of step st+1
+            if (ld) load_a(xn, ph >> 1, i, o);
+            if (mm) mfma_a(ph >> 1, i, o);
+          } else {  // C0, C1 of step st
+            const int qh = 2 * (ph >> 1) + i / NDB, db = i % NDB;
+            if (ld) load_c(xc, qh, db, o);
+            if (mm) mfma_c(qh, db, o);
+          }
+        },
+        [&](int gi) {
+          if (gi == 0) {  // C1(st-1) read block 1's P / dS', which softmax(st, 1) rewrites
+            pin(pb[1][0]); pin(pb[1][1]); pin(dsb[1][0]); pin(dsb[1][1]);
+          }
+          if (gi == 2 * G) {  // C0(st) read block 0's P / dS', which softmax(st+1, 0) rewrites
+            pin(pb[0][0]); pin(pb[0][1]); pin(dsb[0][0]); pin(dsb[0][1]);
+          }
+          const int k = gi % (2 * G);
+#pragma unroll
+          for (int pc = (8 * k) / (2 * G); pc < (8 * (k + 1)) / (2 * G); ++pc) {
+            if (gi < 2 * G) softmax_piece(xc, 1, pc);
+            else softmax_piece(xn, 0, pc);
+          }
+        });
+    wait_loads();  // this wave's copies of tile st+2 have landed
+  }
 
-    // ---- softmax of query block qb in 8 pieces of 2 elements per lane:
-    // P = exp2(S c - L log2 e), dS' = P (scale dP - scale D); masked pairs get 0
-    const bool need_mask = (CAUSAL && q0 < k0 + kBKV) || k0 + kBKV > N;
-    const uint32_t l2_addr = l2_base0 + buf * (kBQ * 4) + (uint32_t)(32 * g);
-    float lv[8], dd[8], pv[8], dv8[8];
-    int dead = 0;
-    auto softmax_piece = [&](int qb, int piece) {
-      const int h = piece >> 2, e0 = 2 * (piece & 3);
-      const uint32_t qr = (uint32_t)(32 * qb + 16 * h);  // + 8 g: 8 consecutive local query rows
-      if ((piece & 3) == 0) {
-        const f32x4 l0 = *(lds_f4*)(uintptr_t)(l2_addr + 4 * qr);
-        const f32x4 l1 = *(lds_f4*)(uintptr_t)(l2_addr + 4 * qr + 16);
-        const f32x4 d0 = *(lds_f4*)(uintptr_t)(l2_addr + kDscMinusL2 + 4 * qr);
-        const f32x4 d1 = *(lds_f4*)(uintptr_t)(l2_addr + kDscMinusL2 + 4 * qr + 16);
+  // ---- last step: C0 with softmax(block 1) beside it, then C1
+  {
+    const Step xc = step_ctx(n_steps - 1);
+    run(G2{},
+        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
+          const int ph = gi / G, i = gi % G;
+          const int qh = 2 * ph + i / NDB, db = i % NDB;
+          if (ld) load_c(xc, qh, db, o);
+          if (mm) mfma_c(qh, db, o);
+        },
+        [&](int gi) {
+          if (gi == 0) {
+            pin(pb[1][0]); pin(pb[1][1]); pin(dsb[1][0]); pin(dsb[1][1]);
+          }
+          if (gi < G)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lv[e] = l0[e];
-          lv[4 + e] = l1[e];
-          dd[e] = d0[e];
-          dd[4 + e] = d1[e];
-        }
-        // masked pairs of this chunk: e < dead (row q0 + qr + 8 g + e sees
-        // key my_key iff my_key <= that row, and only keys below N exist)
-        if (need_mask) {
-          dead = CAUSAL ? my_key - (q0 + (int)qr + 8 * g) : 0;
-          dead = my_key >= N ? 8 : dead;
-        }
-      }
-#pragma unroll
-      for (int e = e0; e < e0 + 2; ++e) {
-        float pe = fast_exp2(fmaf(s[qb][8 * h + e], c, -lv[e]));
-        if (need_mask) pe = e < dead ? 0.f : pe;
-        pv[e] = pe;
-        dv8[e] = pe * fmaf(dp[qb][8 * h + e], scale, -dd[e]);
-      }
-      if ((piece & 3) == 3) {
-        pb[qb][h] = pack_bf16x8(pv);
-        dsb[qb][h] = pack_bf16x8(dv8);
-      }
-    };
-
-    // ---- A0, A1: S = Q K^T and dP = dO V^T, 32 query rows x this wave's 32 keys each
-    load_a(0);
-    load_a(1);
-#pragma unroll
-    for (int ga = 0; ga < NAG; ++ga) {
-      const int qb = ga / NKK, kk = ga % NKK;
-      s[qb] = mfma32(ar[ga % 3][0], kres[kk], kk == 0 ? f32x16{} : s[qb]);
-      dp[qb] = mfma32(ar[ga % 3][1], vres[kk], kk == 0 ? f32x16{} : dp[qb]);
-      anchor_a(s[qb]);
-      anchor_a(dp[qb]);
-      group_fence();
-      if (ga == 0) {  // operands of step st-1's dV / dK products are released
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          pin(at[j][0]);
-          pin(at[j][1]);
-        }
-        pin(pb[1][1]);
-        pin(dsb[1][1]);
-      }
-      pin(ar[(ga + 2) % 3][0]);
-      pin(ar[(ga + 2) % 3][1]);
-      if (ga + 2 < NAG) load_a(ga + 2);
-      if (ga + 2 == NAG) load_c(0);
-      if (ga + 1 == NAG) load_c(1);
-      if (qb == 1) {  // softmax of block 0 while block 1's products run
-#pragma unroll
-        for (int pc = 0; pc < 8 / NKK; ++pc) softmax_piece(0, kk * (8 / NKK) + pc);
-      }
-    }
-
-    // ---- C0, C1: dV^T += dO^T P and dK^T += Q^T dS', contraction over the
-    // query rows; A operands by transpose reads
-#pragma unroll
-    for (int gi = 0; gi < NCG; ++gi) {
-      const int qh = gi / NDB, db = gi % NDB;
-      const int qb = qh >> 1, h = qh & 1;
-      bf16x8(&a)[2] = at[gi % 3];
-      dv_acc[db] = mfma32(a[0], pb[qb][h], dv_acc[db]);
-      dk_acc[db] = mfma32(a[1], dsb[qb][h], dk_acc[db]);
-      anchor_a(dv_acc[db]);
-      anchor_a(dk_acc[db]);
-      group_fence();
-      if (gi == 0) {  // operands of the S / dP products are released
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          pin(ar[j][0]);
-          pin(ar[j][1]);
-        }
-      }
-      if (db == 0 && qh > 0) {  // first group of (qb, h): the previous P / dS' pair is released
-        pin(pb[(qh - 1) >> 1][(qh - 1) & 1]);
-        pin(dsb[(qh - 1) >> 1][(qh - 1) & 1]);
-      }
-      pin(at[(gi + 2) % 3][0]);
-      pin(at[(gi + 2) % 3][1]);
-      if (gi + 2 < NCG) load_c(gi + 2);
-      if (qb == 0) {  // softmax of block 1 while block 0's products run
-#pragma unroll
-        for (int pc = 0; pc < 4 / NDB; ++pc) softmax_piece(1, gi * (4 / NDB) + pc);
-      }
-    }
-    wait_loads();  // this wave's copies of tile st+1 have landed
+            for (int pc = (8 * gi) / G; pc < (8 * (gi + 1)) / G; ++pc) softmax_piece(xc, 1, pc);
+        });
   }
 
   // every MFMA has completed once fin exists: operand registers may be reused
   const float fin = dk_acc[NDB - 1][0] + dv_acc[NDB - 1][0];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    pin(at[j][0], fin);
-    pin(at[j][1], fin);
+  for (int j = 0; j < kSets; ++j) {
+    pin(op[j][0], fin);
+    pin(op[j][1], fin);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {

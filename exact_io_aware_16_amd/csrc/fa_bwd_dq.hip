@@ -14,13 +14,15 @@
 //  * each wave owns 32 query rows; their Q and dO rows stay in registers as
 //    the B operands of S^T = K Q^T and dP^T = V dO^T (keys along M), so a
 //    query's values sit in one lane pair and its L and D are lane scalars;
-//  * K and V tiles of BC keys arrive by LDS-direct buffer loads, double
+//  * K and V tiles of BC keys arrive by LDS-direct buffer loads, triple
 //    buffered, rows in perm32 order with the backward's slot swizzle: the
 //    S^T / dP^T results then hold 8 consecutive keys per register octet --
 //    the B-operand layout of dQ^T += K^T dS'^T -- and the K^T operand is a
 //    transpose read of the same K tile;
 //  * causal: query block qb visits key tiles up to its diagonal only, masks
 //    are applied only on tiles that straddle the diagonal or the ragged end.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 #include "fa_lds.h"
@@ -31,16 +33,23 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;  // query rows per workgroup
+// operand loads run kAhead MFMA groups ahead, through kSets register sets
+constexpr int kAhead = 3;
+constexpr int kSets = kAhead + 1;
 
 template <int D> struct DqTile;
 template <> struct DqTile<128> { static constexpr int BC = 64; };
 template <> struct DqTile<64> { static constexpr int BC = 128; };
 
+// three key tiles in flight: tile t's (dQ products), tile t+1's (S^T / dP^T
+// products) and tile t+2's (arriving)
+constexpr int kTiles = 3;
+
 template <int D>
 struct DqSmem {
   static constexpr int BC = DqTile<D>::BC;
-  bf16_raw k[2][BC * D];  // K tiles: row r holds key perm32(r) of its 32-row group
-  bf16_raw v[2][BC * D];  // V tiles, same layout
+  bf16_raw k[kTiles][BC * D];  // K tiles: row r holds key perm32(r) of its 32-row group
+  bf16_raw v[kTiles][BC * D];  // V tiles, same layout
 };
 
 // 16-byte chunks a thread copies for one BC x D tile: LDS block (i*4 + wave)
@@ -74,7 +83,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   constexpr int NDB = D / 32;   // 32-row blocks of dQ^T
   constexpr int RB = D * 2;     // bytes per row
   constexpr uint32_t kTileBytes = BC * D * 2;
-  constexpr uint32_t kVMinusK = 2 * kTileBytes;  // sm.v[b] - sm.k[b]
+  constexpr uint32_t kVMinusK = kTiles * kTileBytes;  // sm.v[b] - sm.k[b]
   __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
   const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -134,21 +143,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq_acc[db][i] = 0.f;
 
-  // Operand register sets (see pin()).  Each MFMA phase keeps three sets
-  // and loads group g + 2 while group g runs: the set it overwrites was last
-  // read by group g - 1, which has started once group g is issued.
-  //   ar: K and V rows of the S^T and dP^T products (one key block, k-slice)
-  //   at: K^T transpose reads of the dQ product (two head-dim blocks)
-  //   dsb: dS'^T tiles (B operands)
-  constexpr int NAG = NKB * NKK;      // (key block, k-slice) groups of the score phase
-  constexpr int NDG = NKB * NDB;      // (key block, half, pair of head-dim blocks) groups of the dQ phase
-  constexpr int PPA = 8 / NKK;        // softmax pieces per score group
-  constexpr int PPD = 8 / (2 * (NDB / 2));  // softmax pieces per dQ group of key block 0
-  bf16x8 ar[3][2], at[3][2], dsb[NKB][2];
+  // ---- software pipeline over key tiles.  Tile t's work per 32-key block
+  // kb is a score phase S(t, kb) (S^T and dP^T, NKK groups of two MFMAs), a
+  // dQ phase Q(t, kb) (dQ^T += K^T dS'^T, NDB groups of two MFMAs) and the
+  // softmax of the block (dS'^T) on the vector ALUs.  Iteration t runs the
+  // pairs  S(t+1, kb) | Q(t, kb)  for kb = 0 .. NKB-1; beside pair 0 runs the
+  // softmax of tile t's last block, beside pair kb > 0 that of tile t+1's
+  // block kb-1, so every matrix-core phase has independent vector work.  The
+  // prologue runs S(0, *) with the softmax of block kb-1 beside S(0, kb); the
+  // last tile runs Q(*) with its last block's softmax beside the first phases.
+  constexpr int GS = NKK;        // groups of a score phase
+  constexpr int GQ = NDB;        // groups of a dQ phase: (half h, pair of head-dim blocks)
+  constexpr int GP = GS + GQ;    // groups of a pair
+  // Operand ring (see pin()): every group takes two operands -- K and V rows
+  // in score phases, K^T transpose reads of two head-dim blocks in dQ phases.
+  // Group g + kAhead loads into set (g + kAhead) % kSets while group g runs:
+  // that set was last read by group g - 1, which has started once group g is
+  // issued.  Group counts per run are multiples of kSets, so the sets a run
+  // loads first were not read by the previous run's last group.
+  static_assert((NKB * GS) % kSets == 0 && (NKB * GQ) % kSets == 0 && (NKB * GP) % kSets == 0,
+                "operand ring must restart on a run boundary");
+  bf16x8 op[kSets][2], dsb[NKB][2];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) ar[j][0] = ar[j][1] = at[j][0] = at[j][1] = bf16x8{};
+  for (int j = 0; j < kSets; ++j) op[j][0] = op[j][1] = bf16x8{};
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) dsb[kb][0] = dsb[kb][1] = bf16x8{};
+  f32x16 st[NKB], dpt[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) st[kb] = dpt[kb] = f32x16{};
 
   // per-lane LDS address constants (every tile base is a multiple of 1 KiB)
   // row reads: row 32 kb + col, chunk 2 kk + g -> lane constant ^ (32 kk)
@@ -163,115 +185,166 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const uint32_t k_base0 = lds_addr_of(sm.k[0]);
   const int last_key = CAUSAL ? min(my_q, N - 1) : N - 1;  // keys above are masked
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int key0 = t * BC;
-    const uint32_t buf = (uint32_t)(t & 1);
-    // K(t), V(t) have landed (own copies) and are visible (barrier); every
-    // wave is done with tile t-1, whose buffers refill now with tile t+1.
-    wait_loads();
-    __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(buf ^ 1u, key0 + BC);
-    const uint32_t kbase = k_base0 + buf * kTileBytes;
+  // per-tile context: LDS addresses in the tile's buffer, first key, whether
+  // the tile needs masking for this wave's rows
+  struct Tile {
+    uint32_t krow, tk, tk1;
+    int key0;
+    bool mask;
+  };
+  auto tile_ctx = [&](int t) {
+    const uint32_t kbase = k_base0 + (uint32_t)(t % kTiles) * kTileBytes;
+    Tile x;
+    x.krow = opaque(kbase + row_lane);
+    x.tk = opaque(kbase + tk_lane);
+    x.tk1 = opaque(x.tk ^ 32u);  // row + 8: swizzle ^ 2
+    x.key0 = t * BC;
+    x.mask = (CAUSAL && x.key0 + BC - 1 > q0w) || x.key0 + BC > N;
+    return x;
+  };
 
-    // The tile runs as MFMA phases per 32-key block; the softmax of one
-    // block runs on the vector ALUs between the MFMA groups of the next:
-    //   S^T, dP^T of block 0 | of block 1 + softmax(0) | ... |
-    //   dQ from block 0 + softmax(last) | dQ from the other blocks
-    f32x16 st[NKB], dpt[NKB];
-    const uint32_t krow = opaque(kbase + row_lane);
-    auto load_a = [&](int ga) {
-      const int kb = ga / NKK, kk = ga % NKK;
-      const uint32_t ra = (krow ^ (uint32_t)(32 * kk)) + (uint32_t)(32 * kb * RB);
-      ar[ga % 3][0] = lds_row16(ra);
-      ar[ga % 3][1] = lds_row16(ra + kVMinusK);
-    };
-    const uint32_t tk = opaque(kbase + tk_lane);
-    const uint32_t tk1 = opaque(tk ^ 32u);  // row + 8: swizzle ^ 2
-    // dQ group gd = (2 kb + h) (NDB / 2) + pair: head-dim blocks 2 pair, 2 pair + 1
-    auto load_d = [&](int gd) {
-      const int kh = gd / (NDB / 2), pr = gd % (NDB / 2);
-      const uint32_t rows = (uint32_t)(16 * kh * RB);
+  // score group (key block kb, k-slice kk) and dQ group (kh = 2 kb + h,
+  // head-dim blocks 2 pr, 2 pr + 1): operand loads and products
+  auto load_s = [&](const Tile& x, int kb, int kk, bf16x8(&o)[2]) {
+    const uint32_t ra = (x.krow ^ (uint32_t)(32 * kk)) + (uint32_t)(32 * kb * RB);
+    o[0] = lds_row16(ra);
+    o[1] = lds_row16(ra + kVMinusK);
+  };
+  auto load_q = [&](const Tile& x, int kh, int pr, bf16x8(&o)[2]) {
+    const uint32_t rows = (uint32_t)(16 * kh * RB);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int db = 2 * pr + x;
-        at[gd % 3][x] = tr_pair((tk ^ (uint32_t)(64 * db)) + rows, (tk1 ^ (uint32_t)(64 * db)) + rows + 8 * RB);
-      }
-    };
-
-    // dS'^T = P^T (scale dP^T - scale D), P^T = exp2(S^T c - L log2 e), in
-    // 8 pieces of 2 elements per lane; masked pairs get 0
-    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > N;
-    float dsv[8];
-    auto softmax_piece = [&](int kb, int piece) {
-      const int h = piece >> 2, e0 = 2 * (piece & 3);
-      // register 8 h + e of half g holds key key0 + 32 kb + 16 h + 8 g + e
-      const int lim = last_key - (key0 + 32 * kb + 16 * h + 8 * g);
-#pragma unroll
-      for (int e = e0; e < e0 + 2; ++e) {
-        float pe = fast_exp2(fmaf(st[kb][8 * h + e], c, -l2q));
-        if (need_mask) pe = e > lim ? 0.f : pe;
-        dsv[e] = pe * fmaf(dpt[kb][8 * h + e], scale, -dq_sc);
-      }
-      if ((piece & 3) == 3) dsb[kb][h] = pack_bf16x8(dsv);
-    };
-
-    // ---- S^T = K Q^T and dP^T = V dO^T, one 32-key block per phase
-    load_a(0);
-    load_a(1);
-#pragma unroll
-    for (int ga = 0; ga < NAG; ++ga) {
-      const int kb = ga / NKK, kk = ga % NKK;
-      st[kb] = mfma32(ar[ga % 3][0], qf[kk], kk == 0 ? f32x16{} : st[kb]);
-      dpt[kb] = mfma32(ar[ga % 3][1], dof[kk], kk == 0 ? f32x16{} : dpt[kb]);
-      anchor_a(st[kb]);
-      anchor_a(dpt[kb]);
-      group_fence();
-      if (ga == 0) {  // operands of tile t-1's dQ product are released
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          pin(at[j][0]);
-          pin(at[j][1]);
-        }
-        pin(dsb[NKB - 1][1]);
-      }
-      pin(ar[(ga + 2) % 3][0]);
-      pin(ar[(ga + 2) % 3][1]);
-      if (ga + 2 < NAG) load_a(ga + 2);
-      if (ga + 2 == NAG) load_d(0);
-      if (ga + 1 == NAG) load_d(1);
-      if (kb > 0) {  // softmax of the previous block
-#pragma unroll
-        for (int pc = 0; pc < PPA; ++pc) softmax_piece(kb - 1, kk * PPA + pc);
-      }
+    for (int y = 0; y < 2; ++y) {
+      const int db = 2 * pr + y;
+      o[y] = tr_pair((x.tk ^ (uint32_t)(64 * db)) + rows, (x.tk1 ^ (uint32_t)(64 * db)) + rows + 8 * RB);
     }
-
-    // ---- dQ^T += K^T dS'^T, K^T by transpose reads of the K tile
+  };
+  auto mfma_s = [&](int kb, int kk, const bf16x8(&o)[2]) {
+    st[kb] = mfma32(o[0], qf[kk], kk == 0 ? f32x16{} : st[kb]);
+    dpt[kb] = mfma32(o[1], dof[kk], kk == 0 ? f32x16{} : dpt[kb]);
+    anchor_a(st[kb]);
+    anchor_a(dpt[kb]);
+  };
+  auto mfma_q = [&](int kh, int pr, const bf16x8(&o)[2]) {
 #pragma unroll
-    for (int gd = 0; gd < NDG; ++gd) {
-      const int kh = gd / (NDB / 2), pr = gd % (NDB / 2);
-      const int kb = kh >> 1, h = kh & 1;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        dq_acc[2 * pr + x] = mfma32(at[gd % 3][x], dsb[kb][h], dq_acc[2 * pr + x]);
-        anchor_a(dq_acc[2 * pr + x]);
-      }
-      group_fence();
-      if (gd == 0) {  // operands of the score products are released
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          pin(ar[j][0]);
-          pin(ar[j][1]);
-        }
-      }
-      if (pr == 0 && kh > 0) pin(dsb[(kh - 1) >> 1][(kh - 1) & 1]);  // the previous dS' group is released
-      pin(at[(gd + 2) % 3][0]);
-      pin(at[(gd + 2) % 3][1]);
-      if (gd + 2 < NDG) load_d(gd + 2);
-      if (kb == 0) {  // softmax of the last block
-#pragma unroll
-        for (int pc = 0; pc < PPD; ++pc) softmax_piece(NKB - 1, gd * PPD + pc);
-      }
+    for (int y = 0; y < 2; ++y) {
+      dq_acc[2 * pr + y] = mfma32(o[y], dsb[kh >> 1][kh & 1], dq_acc[2 * pr + y]);
+      anchor_a(dq_acc[2 * pr + y]);
     }
+  };
+  // group i of a dQ phase: half h = i / (NDB / 2), pair pr = i % (NDB / 2)
+  auto q_kh = [&](int kb, int i) { return 2 * kb + i / (NDB / 2); };
+  auto q_pr = [&](int i) { return i % (NDB / 2); };
+
+  // dS'^T = P^T (scale dP^T - scale D), P^T = exp2(S^T c - L log2 e), in
+  // 8 pieces of 2 elements per lane; masked pairs get 0
+  float dsv[8];
+  auto softmax_piece = [&](const Tile& x, int kb, int piece) {
+    const int h = piece >> 2, e0 = 2 * (piece & 3);
+    // register 8 h + e of half g holds key key0 + 32 kb + 16 h + 8 g + e
+    const int lim = last_key - (x.key0 + 32 * kb + 16 * h + 8 * g);
+#pragma unroll
+    for (int e = e0; e < e0 + 2; ++e) {
+      float pe = fast_exp2(fmaf(st[kb][8 * h + e], c, -l2q));
+      if (x.mask) pe = e > lim ? 0.f : pe;
+      dsv[e] = pe * fmaf(dpt[kb][8 * h + e], scale, -dq_sc);
+    }
+    if ((piece & 3) == 3) dsb[kb][h] = pack_bf16x8(dsv);
+  };
+  // the pieces of 8 that go beside group k of n
+  auto pieces = [&](const Tile& x, int kb, int k, int n) {
+#pragma unroll
+    for (int pc = (8 * k) / n; pc < (8 * (k + 1)) / n; ++pc) softmax_piece(x, kb, pc);
+  };
+  // dQ products of tile t-1 read block kb's dS', which the softmax of tile t
+  // rewrites: keep the old value alive past the first group of the next run
+  auto release_ds = [&](int kb) {
+    pin(dsb[kb][0]);
+    pin(dsb[kb][1]);
+  };
+
+  // ---- one run of NG groups.  group(gi, ld, mm, o) loads group gi's
+  // operands into o (ld) or issues its products from o (mm); between(gi)
+  // runs vector work after group gi has issued.  At gi = 0 the ring pin
+  // keeps the set read by the previous run's last group alive past the
+  // run's first product, so no preamble load reuses its registers.
+  auto run = [&](auto n_groups, auto group, auto between) {
+    constexpr int NG = decltype(n_groups)::value;
+#pragma unroll
+    for (int gi = 0; gi < kAhead; ++gi) group(gi, true, false, op[gi % kSets]);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      group(gi, false, true, op[gi % kSets]);
+      group_fence();
+      pin(op[(gi + kAhead) % kSets][0]);
+      pin(op[(gi + kAhead) % kSets][1]);
+      if (gi + kAhead < NG) group(gi + kAhead, true, false, op[(gi + kAhead) % kSets]);
+      between(gi);
+    }
+  };
+
+  // ---- prologue: S(0, *) with the softmax of block kb-1 beside S(0, kb)
+  wait_loads();
+  __syncthreads();  // tile 0 visible
+  if (n_tiles > 1) issue_tile(1u, BC);
+  {
+    const Tile x0 = tile_ctx(0);
+    run(std::integral_constant<int, NKB * GS>{},
+        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
+          if (ld) load_s(x0, gi / GS, gi % GS, o);
+          if (mm) mfma_s(gi / GS, gi % GS, o);
+        },
+        [&](int gi) {
+          if (gi >= GS) pieces(x0, gi / GS - 1, gi % GS, GS);
+        });
+  }
+  wait_loads();  // this wave's copies of tile 1 have landed
+
+  // ---- steady state: S(t+1, kb) | Q(t, kb) for every block kb
+  for (int t = 0; t + 1 < n_tiles; ++t) {
+    __syncthreads();  // tile t+1 visible; every wave is done with tile t-1
+    if (t + 2 < n_tiles) issue_tile((uint32_t)((t + 2) % kTiles), (t + 2) * BC);
+    const Tile xc = tile_ctx(t), xn = tile_ctx(t + 1);
+    run(std::integral_constant<int, NKB * GP>{},
+        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
+          const int kb = gi / GP, i = gi % GP;
+          if (i < GS) {
+            if (ld) load_s(xn, kb, i, o);
+            if (mm) mfma_s(kb, i, o);
+          } else {
+            if (ld) load_q(xc, q_kh(kb, i - GS), q_pr(i - GS), o);
+            if (mm) mfma_q(q_kh(kb, i - GS), q_pr(i - GS), o);
+          }
+        },
+        [&](int gi) {
+          const int kb = gi / GP, i = gi % GP;
+          if (i == 0) release_ds(kb == 0 ? NKB - 1 : kb - 1);
+          if (kb == 0) pieces(xc, NKB - 1, i, GP);
+          else pieces(xn, kb - 1, i, GP);
+        });
+    wait_loads();  // this wave's copies of tile t+2 have landed
+  }
+
+  // ---- last tile: Q(*), its last block's softmax beside the phases before
+  // the last one
+  {
+    const Tile xc = tile_ctx(n_tiles - 1);
+    constexpr int NSM = (NKB - 1) * GQ;  // groups that carry the softmax
+    run(std::integral_constant<int, NKB * GQ>{},
+        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
+          const int kb = gi / GQ, i = gi % GQ;
+          if (ld) load_q(xc, q_kh(kb, i), q_pr(i), o);
+          if (mm) mfma_q(q_kh(kb, i), q_pr(i), o);
+        },
+        [&](int gi) {
+          if (gi == 0) {
+            release_ds(NKB - 1);
+            // with a single tile the prologue's last score product precedes
+            // this run: its Q / dO operands stay unwritten until now
+            pin(qf[NKK - 1]);
+            pin(dof[NKK - 1]);
+          }
+          if (gi < NSM) pieces(xc, NKB - 1, gi, NSM);
+        });
   }
 
   // every MFMA has completed once fin exists: operand registers may be reused
@@ -279,9 +352,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 #pragma unroll
   for (int db = 0; db < NDB; ++db) fin += dq_acc[db][0];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    pin(at[j][0], fin);
-    pin(at[j][1], fin);
+  for (int j = 0; j < kSets; ++j) {
+    pin(op[j][0], fin);
+    pin(op[j][1], fin);
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
