@@ -41,8 +41,6 @@
 //  the transpose reads of a tile without LDS bank conflicts; every per-lane
 //  LDS address is a lane constant XOR a compile-time mask, plus an
 //  immediate.
-#include <type_traits>
-
 #include "fa_common.h"
 #include "fa_launch.h"
 #include "fa_lds.h"
@@ -248,12 +246,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const uint32_t q_base0 = lds_addr_of(sm.q[0]);
   const uint32_t l2_base0 = lds_addr_of(sm.l2[0]);
 
-  // per-step context: LDS addresses in the step's tile buffer, first query
-  // row, whether the step's pairs need masking
+  // per-step context: LDS addresses in the step's tile buffer, first query row
   struct Step {
     uint32_t qrow, tq, tq1, l2;
     int q0;
-    bool mask;
   };
   auto step_ctx = [&](int st) {
     const uint32_t b = (uint32_t)(st % kTiles);
@@ -264,7 +260,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     x.tq1 = opaque(x.tq ^ 32u);  // row + 8: swizzle ^ 2
     x.l2 = l2_base0 + b * (kBQ * 4) + (uint32_t)(32 * g);
     x.q0 = q_first + st * kBQ;
-    x.mask = (CAUSAL && x.q0 < k0 + kBKV) || k0 + kBKV > N;
     return x;
   };
 
@@ -295,67 +290,92 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     anchor_a(dk_acc[db]);
   };
 
-  // ---- softmax of query block qb of a step in 8 pieces of 2 elements per
+  // ---- softmax of query block qb of a step, in 8 pieces of 2 elements per
   // lane: P = exp2(S c - L log2 e), dS' = P (scale dP - scale D); masked
-  // pairs get 0.  Chunk h = piece / 4 covers 8 consecutive query rows.
-  float lv[8], dd[8], pv[8], dv8[8];
+  // pairs get 0.  Chunk h = piece / 4 covers 8 consecutive query rows.  Its
+  // L log2 e and scale D (lvd[h]) are read from LDS one chunk ahead, so the
+  // reads never hold up the operand loads queued behind them.  `masked` is
+  // a compile-time flag: steps off the diagonal and inside the sequence
+  // take the code without masks.
+  float lvd[2][16], pv[8], dv8[8];
   int dead = 0;
-  auto softmax_piece = [&](const Step& x, int qb, int piece) {
-    const int h = piece >> 2, e0 = 2 * (piece & 3);
-    const uint32_t qr = (uint32_t)(32 * qb + 16 * h);  // + 8 g: 8 consecutive local query rows
-    if ((piece & 3) == 0) {
-      const f32x4 l0 = *(lds_f4*)(uintptr_t)(x.l2 + 4 * qr);
-      const f32x4 l1 = *(lds_f4*)(uintptr_t)(x.l2 + 4 * qr + 16);
-      const f32x4 d0 = *(lds_f4*)(uintptr_t)(x.l2 + kDscMinusL2 + 4 * qr);
-      const f32x4 d1 = *(lds_f4*)(uintptr_t)(x.l2 + kDscMinusL2 + 4 * qr + 16);
+  // L log2 e and scale D of chunk h of block qb of step x into lvd[h]
+  auto load_ld = [&](const Step& x, int qb, auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const uint32_t a = x.l2 + 4u * (uint32_t)(32 * qb + 16 * h);
+    const f32x4 l0 = *(lds_f4*)(uintptr_t)a;
+    const f32x4 l1 = *(lds_f4*)(uintptr_t)(a + 16);
+    const f32x4 d0 = *(lds_f4*)(uintptr_t)(a + kDscMinusL2);
+    const f32x4 d1 = *(lds_f4*)(uintptr_t)(a + kDscMinusL2 + 16);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lv[e] = l0[e];
-        lv[4 + e] = l1[e];
-        dd[e] = d0[e];
-        dd[4 + e] = d1[e];
-      }
-      // masked pairs of this chunk: e < dead (row q0 + qr + 8 g + e sees
-      // key my_key iff my_key <= that row, and only keys below N exist)
-      if (x.mask) {
-        dead = CAUSAL ? my_key - (x.q0 + (int)qr + 8 * g) : 0;
+    for (int e = 0; e < 4; ++e) {
+      lvd[h][e] = l0[e];
+      lvd[h][4 + e] = l1[e];
+      lvd[h][8 + e] = d0[e];
+      lvd[h][12 + e] = d1[e];
+    }
+  };
+  // piece pc of block (x, qb); (xn, qbn) is the block whose softmax follows
+  // (none when !has_next)
+  auto softmax_piece = [&](const Step& x, int qb, auto pc, auto masked, const Step& xn, int qbn, bool has_next) {
+    constexpr int piece = decltype(pc)::value, h = piece >> 2, e0 = 2 * (piece & 3);
+    constexpr bool M = decltype(masked)::value;
+    if constexpr ((piece & 3) == 0) {
+      if constexpr (h == 0) load_ld(x, qb, ic<1>{});
+      else if (has_next) load_ld(xn, qbn, ic<0>{});
+      // masked pairs of this chunk: e < dead (row q0 + 32 qb + 16 h + 8 g + e
+      // sees key my_key iff my_key <= that row, and only keys below N exist)
+      if constexpr (M) {
+        dead = CAUSAL ? my_key - (x.q0 + 32 * qb + 16 * h + 8 * g) : 0;
         dead = my_key >= N ? 8 : dead;
       }
     }
 #pragma unroll
     for (int e = e0; e < e0 + 2; ++e) {
-      float pe = fast_exp2(fmaf(s[qb][8 * h + e], c, -lv[e]));
-      if (x.mask) pe = e < dead ? 0.f : pe;
+      float pe = fast_exp2(fmaf(s[qb][8 * h + e], c, -lvd[h][e]));
+      if constexpr (M) pe = e < dead ? 0.f : pe;
       pv[e] = pe;
-      dv8[e] = pe * fmaf(dp[qb][8 * h + e], scale, -dd[e]);
+      dv8[e] = pe * fmaf(dp[qb][8 * h + e], scale, -lvd[h][8 + e]);
     }
-    if ((piece & 3) == 3) {
+    if constexpr ((piece & 3) == 3) {
       pb[qb][h] = pack_bf16x8(pv);
       dsb[qb][h] = pack_bf16x8(dv8);
     }
   };
-
-  // ---- one run of NG groups.  group(gi, ld, mm, o) loads group gi's
-  // operands into o (ld) or issues its products from o (mm); between(gi)
-  // runs vector work after group gi has issued.  At gi = 0 the ring pin
-  // keeps the set read by the previous run's last group alive past the
-  // run's first product, so no preamble load reuses its registers.
-  auto run = [&](auto n_groups, auto group, auto between) {
-    constexpr int NG = decltype(n_groups)::value;
-#pragma unroll
-    for (int gi = 0; gi < kAhead; ++gi) group(gi, true, false, op[gi % kSets]);
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      group(gi, false, true, op[gi % kSets]);
-      group_fence();
-      pin(op[(gi + kAhead) % kSets][0]);
-      pin(op[(gi + kAhead) % kSets][1]);
-      if (gi + kAhead < NG) group(gi + kAhead, true, false, op[(gi + kAhead) % kSets]);
-      between(gi);
-    }
+  // the softmax pieces of 8 that go beside group k of n
+  auto pieces = [&](auto k, auto n, auto&& piece) {
+    constexpr int K = decltype(k)::value, Nn = decltype(n)::value;
+    static_for<(8 * K) / Nn, (8 * (K + 1)) / Nn>(piece);
   };
-  using G2 = std::integral_constant<int, 2 * G>;
-  using G4 = std::integral_constant<int, 4 * G>;
+  // the products of the previous run read block qb's P / dS', which the
+  // softmax beside this run rewrites
+  auto release_p = [&](int qb) {
+    pin(pb[qb][0]);
+    pin(pb[qb][1]);
+    pin(dsb[qb][0]);
+    pin(dsb[qb][1]);
+  };
+
+  // ---- one run of NG groups.  load(gi, o) loads group gi's operands into o,
+  // mfma(gi, o) issues its products; between(gi) runs vector work after
+  // group gi has issued.  At gi = 0 the ring pin keeps the set read by the
+  // previous run's last group alive past the run's first product, so no
+  // preamble load reuses its registers.
+  auto run = [&](auto n_groups, auto load, auto mfma, auto between) {
+    constexpr int NG = decltype(n_groups)::value;
+    static_for<0, kAhead>([&](auto gi) { load(gi, op[decltype(gi)::value % kSets]); });
+    static_for<0, NG>([&](auto gi) {
+      constexpr int n = decltype(gi)::value, nxt = (n + kAhead) % kSets;
+      mfma(gi, op[n % kSets]);
+      group_fence();
+      pin(op[nxt][0]);
+      pin(op[nxt][1]);
+      if constexpr (n + kAhead < NG) load(ic<n + kAhead>{}, op[nxt]);
+      between(gi);
+    });
+  };
+  const std::true_type with_masks;
+  const std::false_type no_masks;
 
   // ---- prologue: A0(0), A1(0) with softmax(0, block 0) beside A1
   wait_loads();
@@ -363,71 +383,69 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   if (n_steps > 1) issue_qtile(1u, q_first + kBQ);
   {
     const Step x0 = step_ctx(0);
-    run(G2{},
-        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
-          const int qb = gi / G, kk = gi % G;
-          if (ld) load_a(x0, qb, kk, o);
-          if (mm) mfma_a(qb, kk, o);
-        },
-        [&](int gi) {
-          if (gi >= G)
-#pragma unroll
-            for (int pc = (8 * (gi - G)) / G; pc < (8 * (gi - G + 1)) / G; ++pc) softmax_piece(x0, 0, pc);
+    load_ld(x0, 0, ic<0>{});
+    run(ic<2 * G>{},
+        [&](auto gi, bf16x8(&o)[2]) { load_a(x0, gi / G, gi % G, o); },
+        [&](auto gi, const bf16x8(&o)[2]) { mfma_a(gi / G, gi % G, o); },
+        [&](auto gi) {
+          constexpr int n = decltype(gi)::value;
+          if constexpr (n >= G)
+            pieces(ic<n - G>{}, ic<G>{}, [&](auto pc) { softmax_piece(x0, 0, pc, with_masks, x0, 1, true); });
         });
   }
   wait_loads();  // this wave's copies of tile 1 have landed
 
-  // ---- steady state: A0(st+1) | C0(st) | A1(st+1) | C1(st)
-  for (int st = 0; st + 1 < n_steps; ++st) {
+  // ---- steady state: A0(st+1) | C0(st) | A1(st+1) | C1(st), softmax(st, 1)
+  // beside the first two phases and softmax(st+1, 0) beside the last two
+  auto iterate = [&](const Step& xc, const Step& xn, auto masked) {
+    run(ic<4 * G>{},
+        [&](auto gi, bf16x8(&o)[2]) {
+          constexpr int n = decltype(gi)::value, ph = n / G, i = n % G;
+          if constexpr (ph == 0 || ph == 2) load_a(xn, ph >> 1, i, o);   // A0, A1 of step st+1
+          else load_c(xc, 2 * (ph >> 1) + i / NDB, i % NDB, o);          // C0, C1 of step st
+        },
+        [&](auto gi, const bf16x8(&o)[2]) {
+          constexpr int n = decltype(gi)::value, ph = n / G, i = n % G;
+          if constexpr (ph == 0 || ph == 2) mfma_a(ph >> 1, i, o);
+          else mfma_c(2 * (ph >> 1) + i / NDB, i % NDB, o);
+        },
+        [&](auto gi) {
+          constexpr int n = decltype(gi)::value;
+          if constexpr (n == 0) release_p(1);      // read by C1(st-1)
+          if constexpr (n == 2 * G) release_p(0);  // read by C0(st)
+          if constexpr (n < 2 * G)
+            pieces(ic<n>{}, ic<2 * G>{}, [&](auto pc) { softmax_piece(xc, 1, pc, masked, xn, 0, true); });
+          else
+            pieces(ic<n - 2 * G>{}, ic<2 * G>{}, [&](auto pc) { softmax_piece(xn, 0, pc, masked, xn, 1, true); });
+        });
+  };
+  auto step = [&](int st, auto masked) {
     __syncthreads();  // tile st+1 visible; every wave is done with tile st-1
     if (st + 2 < n_steps) issue_qtile((uint32_t)((st + 2) % kTiles), q_first + (st + 2) * kBQ);
-    const Step xc = step_ctx(st), xn = step_ctx(st + 1);
-    run(G4{},
-        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
-          const int ph = gi / G, i = gi % G;
-          if (ph == 0 || ph == 2) {  // A0, A1 of step st+1
-            if (ld) load_a(xn, ph >> 1, i, o);
-            if (mm) mfma_a(ph >> 1, i, o);
-          } else {  // C0, C1 of step st
-            const int qh = 2 * (ph >> 1) + i / NDB, db = i % NDB;
-            if (ld) load_c(xc, qh, db, o);
-            if (mm) mfma_c(qh, db, o);
-          }
-        },
-        [&](int gi) {
-          if (gi == 0) {  // C1(st-1) read block 1's P / dS', which softmax(st, 1) rewrites
-            pin(pb[1][0]); pin(pb[1][1]); pin(dsb[1][0]); pin(dsb[1][1]);
-          }
-          if (gi == 2 * G) {  // C0(st) read block 0's P / dS', which softmax(st+1, 0) rewrites
-            pin(pb[0][0]); pin(pb[0][1]); pin(dsb[0][0]); pin(dsb[0][1]);
-          }
-          const int k = gi % (2 * G);
-#pragma unroll
-          for (int pc = (8 * k) / (2 * G); pc < (8 * (k + 1)) / (2 * G); ++pc) {
-            if (gi < 2 * G) softmax_piece(xc, 1, pc);
-            else softmax_piece(xn, 0, pc);
-          }
-        });
+    iterate(step_ctx(st), step_ctx(st + 1), masked);
     wait_loads();  // this wave's copies of tile st+2 have landed
-  }
+  };
+  // Steps that need masks form a prefix: the ones that meet the diagonal, or
+  // all of them in the block that holds the end of the sequence.  Iteration
+  // st touches steps st and st+1, so it needs masks iff st < n_mask.  Two
+  // loops rather than a branch per iteration keep one register assignment
+  // per loop body.
+  const int n_mask = k0 + kBKV > N ? n_steps : CAUSAL ? min(n_steps, (k0 + kBKV - q_first + kBQ - 1) / kBQ) : 0;
+  int st = 0;
+  for (; st + 1 < n_steps && st < n_mask; ++st) step(st, with_masks);
+  for (; st + 1 < n_steps; ++st) step(st, no_masks);
 
   // ---- last step: C0 with softmax(block 1) beside it, then C1
   {
     const Step xc = step_ctx(n_steps - 1);
-    run(G2{},
-        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
-          const int ph = gi / G, i = gi % G;
-          const int qh = 2 * ph + i / NDB, db = i % NDB;
-          if (ld) load_c(xc, qh, db, o);
-          if (mm) mfma_c(qh, db, o);
-        },
-        [&](int gi) {
-          if (gi == 0) {
-            pin(pb[1][0]); pin(pb[1][1]); pin(dsb[1][0]); pin(dsb[1][1]);
-          }
-          if (gi < G)
-#pragma unroll
-            for (int pc = (8 * gi) / G; pc < (8 * (gi + 1)) / G; ++pc) softmax_piece(xc, 1, pc);
+    run(ic<2 * G>{},
+        [&](auto gi, bf16x8(&o)[2]) { load_c(xc, 2 * (gi / G) + (gi % G) / NDB, (gi % G) % NDB, o); },
+        [&](auto gi, const bf16x8(&o)[2]) { mfma_c(2 * (gi / G) + (gi % G) / NDB, (gi % G) % NDB, o); },
+        [&](auto gi) {
+          constexpr int n = decltype(gi)::value;
+          if constexpr (n == 0) release_p(1);
+          if constexpr (n < G)
+            pieces(ic<n>{}, ic<G>{}, [&](auto pc) { softmax_piece(xc, 1, pc, with_masks, xc, 0, false); });
         });
   }
 

@@ -17,7 +17,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Compile-time loop: f(ic<i>{}) for i = B .. E-1.  Group, phase and piece
+// indices of the backward kernels go through this rather than through
+// unrolled loops, so every register-array index is a constant from the start.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(ic<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
