@@ -21,8 +21,6 @@
 //    transpose read of the same K tile;
 //  * causal: query block qb visits key tiles up to its diagonal only, masks
 //    are applied only on tiles that straddle the diagonal or the ragged end.
-#include <type_traits>
-
 #include "fa_common.h"
 #include "fa_launch.h"
 #include "fa_lds.h"
@@ -185,12 +183,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const uint32_t k_base0 = lds_addr_of(sm.k[0]);
   const int last_key = CAUSAL ? min(my_q, N - 1) : N - 1;  // keys above are masked
 
-  // per-tile context: LDS addresses in the tile's buffer, first key, whether
-  // the tile needs masking for this wave's rows
+  // per-tile context: LDS addresses in the tile's buffer, first key
   struct Tile {
     uint32_t krow, tk, tk1;
     int key0;
-    bool mask;
   };
   auto tile_ctx = [&](int t) {
     const uint32_t kbase = k_base0 + (uint32_t)(t % kTiles) * kTileBytes;
@@ -199,7 +195,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     x.tk = opaque(kbase + tk_lane);
     x.tk1 = opaque(x.tk ^ 32u);  // row + 8: swizzle ^ 2
     x.key0 = t * BC;
-    x.mask = (CAUSAL && x.key0 + BC - 1 > q0w) || x.key0 + BC > N;
     return x;
   };
 
@@ -236,24 +231,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   auto q_pr = [&](int i) { return i % (NDB / 2); };
 
   // dS'^T = P^T (scale dP^T - scale D), P^T = exp2(S^T c - L log2 e), in
-  // 8 pieces of 2 elements per lane; masked pairs get 0
+  // 8 pieces of 2 elements per lane; masked pairs get 0.  `masked` is a
+  // compile-time flag: tiles below the diagonal and inside the sequence take
+  // the code without masks.
   float dsv[8];
-  auto softmax_piece = [&](const Tile& x, int kb, int piece) {
-    const int h = piece >> 2, e0 = 2 * (piece & 3);
+  auto softmax_piece = [&](const Tile& x, int kb, auto pc, auto masked) {
+    constexpr int piece = decltype(pc)::value, h = piece >> 2, e0 = 2 * (piece & 3);
     // register 8 h + e of half g holds key key0 + 32 kb + 16 h + 8 g + e
-    const int lim = last_key - (x.key0 + 32 * kb + 16 * h + 8 * g);
+    int lim = 0;
+    if constexpr (decltype(masked)::value) lim = last_key - (x.key0 + 32 * kb + 16 * h + 8 * g);
 #pragma unroll
     for (int e = e0; e < e0 + 2; ++e) {
       float pe = fast_exp2(fmaf(st[kb][8 * h + e], c, -l2q));
-      if (x.mask) pe = e > lim ? 0.f : pe;
+      if constexpr (decltype(masked)::value) pe = e > lim ? 0.f : pe;
       dsv[e] = pe * fmaf(dpt[kb][8 * h + e], scale, -dq_sc);
     }
-    if ((piece & 3) == 3) dsb[kb][h] = pack_bf16x8(dsv);
+    if constexpr ((piece & 3) == 3) dsb[kb][h] = pack_bf16x8(dsv);
   };
-  // the pieces of 8 that go beside group k of n
-  auto pieces = [&](const Tile& x, int kb, int k, int n) {
-#pragma unroll
-    for (int pc = (8 * k) / n; pc < (8 * (k + 1)) / n; ++pc) softmax_piece(x, kb, pc);
+  // the softmax pieces of 8 that go beside group k of n
+  auto pieces = [&](auto k, auto n, auto&& piece) {
+    constexpr int K = decltype(k)::value, Nn = decltype(n)::value;
+    static_for<(8 * K) / Nn, (8 * (K + 1)) / Nn>(piece);
   };
   // dQ products of tile t-1 read block kb's dS', which the softmax of tile t
   // rewrites: keep the old value alive past the first group of the next run
@@ -262,25 +260,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     pin(dsb[kb][1]);
   };
 
-  // ---- one run of NG groups.  group(gi, ld, mm, o) loads group gi's
-  // operands into o (ld) or issues its products from o (mm); between(gi)
-  // runs vector work after group gi has issued.  At gi = 0 the ring pin
-  // keeps the set read by the previous run's last group alive past the
-  // run's first product, so no preamble load reuses its registers.
-  auto run = [&](auto n_groups, auto group, auto between) {
+  // ---- one run of NG groups.  load(gi, o) loads group gi's operands into o,
+  // mfma(gi, o) issues its products; between(gi) runs vector work after
+  // group gi has issued.  At gi = 0 the ring pin keeps the set read by the
+  // previous run's last group alive past the run's first product, so no
+  // preamble load reuses its registers.
+  auto run = [&](auto n_groups, auto load, auto mfma, auto between) {
     constexpr int NG = decltype(n_groups)::value;
-#pragma unroll
-    for (int gi = 0; gi < kAhead; ++gi) group(gi, true, false, op[gi % kSets]);
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      group(gi, false, true, op[gi % kSets]);
+    static_for<0, kAhead>([&](auto gi) { load(gi, op[decltype(gi)::value % kSets]); });
+    static_for<0, NG>([&](auto gi) {
+      constexpr int n = decltype(gi)::value, nxt = (n + kAhead) % kSets;
+      mfma(gi, op[n % kSets]);
       group_fence();
-      pin(op[(gi + kAhead) % kSets][0]);
-      pin(op[(gi + kAhead) % kSets][1]);
-      if (gi + kAhead < NG) group(gi + kAhead, true, false, op[(gi + kAhead) % kSets]);
+      pin(op[nxt][0]);
+      pin(op[nxt][1]);
+      if constexpr (n + kAhead < NG) load(ic<n + kAhead>{}, op[nxt]);
       between(gi);
-    }
+    });
   };
+  const std::true_type with_masks;
+  const std::false_type no_masks;
 
   // ---- prologue: S(0, *) with the softmax of block kb-1 beside S(0, kb)
   wait_loads();
@@ -288,62 +287,72 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   if (n_tiles > 1) issue_tile(1u, BC);
   {
     const Tile x0 = tile_ctx(0);
-    run(std::integral_constant<int, NKB * GS>{},
-        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
-          if (ld) load_s(x0, gi / GS, gi % GS, o);
-          if (mm) mfma_s(gi / GS, gi % GS, o);
-        },
-        [&](int gi) {
-          if (gi >= GS) pieces(x0, gi / GS - 1, gi % GS, GS);
+    run(ic<NKB * GS>{},
+        [&](auto gi, bf16x8(&o)[2]) { load_s(x0, gi / GS, gi % GS, o); },
+        [&](auto gi, const bf16x8(&o)[2]) { mfma_s(gi / GS, gi % GS, o); },
+        [&](auto gi) {
+          constexpr int n = decltype(gi)::value;
+          if constexpr (n >= GS)
+            pieces(ic<n % GS>{}, ic<GS>{}, [&](auto pc) { softmax_piece(x0, n / GS - 1, pc, with_masks); });
         });
   }
   wait_loads();  // this wave's copies of tile 1 have landed
 
   // ---- steady state: S(t+1, kb) | Q(t, kb) for every block kb
-  for (int t = 0; t + 1 < n_tiles; ++t) {
+  auto iterate = [&](const Tile& xc, const Tile& xn, auto masked) {
+    run(ic<NKB * GP>{},
+        [&](auto gi, bf16x8(&o)[2]) {
+          constexpr int n = decltype(gi)::value, kb = n / GP, i = n % GP;
+          if constexpr (i < GS) load_s(xn, kb, i, o);
+          else load_q(xc, q_kh(kb, i - GS), q_pr(i - GS), o);
+        },
+        [&](auto gi, const bf16x8(&o)[2]) {
+          constexpr int n = decltype(gi)::value, kb = n / GP, i = n % GP;
+          if constexpr (i < GS) mfma_s(kb, i, o);
+          else mfma_q(q_kh(kb, i - GS), q_pr(i - GS), o);
+        },
+        [&](auto gi) {
+          constexpr int n = decltype(gi)::value, kb = n / GP, i = n % GP;
+          if constexpr (i == 0) release_ds(kb == 0 ? NKB - 1 : kb - 1);
+          if constexpr (kb == 0)
+            pieces(ic<i>{}, ic<GP>{}, [&](auto pc) { softmax_piece(xc, NKB - 1, pc, masked); });
+          else
+            pieces(ic<i>{}, ic<GP>{}, [&](auto pc) { softmax_piece(xn, kb - 1, pc, masked); });
+        });
+  };
+  auto step = [&](int t, auto masked) {
     __syncthreads();  // tile t+1 visible; every wave is done with tile t-1
     if (t + 2 < n_tiles) issue_tile((uint32_t)((t + 2) % kTiles), (t + 2) * BC);
-    const Tile xc = tile_ctx(t), xn = tile_ctx(t + 1);
-    run(std::integral_constant<int, NKB * GP>{},
-        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
-          const int kb = gi / GP, i = gi % GP;
-          if (i < GS) {
-            if (ld) load_s(xn, kb, i, o);
-            if (mm) mfma_s(kb, i, o);
-          } else {
-            if (ld) load_q(xc, q_kh(kb, i - GS), q_pr(i - GS), o);
-            if (mm) mfma_q(q_kh(kb, i - GS), q_pr(i - GS), o);
-          }
-        },
-        [&](int gi) {
-          const int kb = gi / GP, i = gi % GP;
-          if (i == 0) release_ds(kb == 0 ? NKB - 1 : kb - 1);
-          if (kb == 0) pieces(xc, NKB - 1, i, GP);
-          else pieces(xn, kb - 1, i, GP);
-        });
+    iterate(tile_ctx(t), tile_ctx(t + 1), masked);
     wait_loads();  // this wave's copies of tile t+2 have landed
-  }
+  };
+  // Tiles that need masks (for any row of the workgroup) form a suffix: the
+  // ones that meet the diagonal and the one holding the end of the sequence.
+  // Iteration t touches tiles t and t+1, so it needs masks iff t+1 >= t_mask.
+  const int t_mask = min(CAUSAL ? (q_start + 1) / BC : n_tiles, N / BC);
+  int t = 0;
+  for (; t + 1 < n_tiles && t + 1 < t_mask; ++t) step(t, no_masks);
+  for (; t + 1 < n_tiles; ++t) step(t, with_masks);
 
   // ---- last tile: Q(*), its last block's softmax beside the phases before
   // the last one
   {
     const Tile xc = tile_ctx(n_tiles - 1);
     constexpr int NSM = (NKB - 1) * GQ;  // groups that carry the softmax
-    run(std::integral_constant<int, NKB * GQ>{},
-        [&](int gi, bool ld, bool mm, bf16x8(&o)[2]) {
-          const int kb = gi / GQ, i = gi % GQ;
-          if (ld) load_q(xc, q_kh(kb, i), q_pr(i), o);
-          if (mm) mfma_q(q_kh(kb, i), q_pr(i), o);
-        },
-        [&](int gi) {
-          if (gi == 0) {
+    run(ic<NKB * GQ>{},
+        [&](auto gi, bf16x8(&o)[2]) { load_q(xc, q_kh(gi / GQ, gi % GQ), q_pr(gi % GQ), o); },
+        [&](auto gi, const bf16x8(&o)[2]) { mfma_q(q_kh(gi / GQ, gi % GQ), q_pr(gi % GQ), o); },
+        [&](auto gi) {
+          constexpr int n = decltype(gi)::value;
+          if constexpr (n == 0) {
             release_ds(NKB - 1);
             // with a single tile the prologue's last score product precedes
             // this run: its Q / dO operands stay unwritten until now
             pin(qf[NKK - 1]);
             pin(dof[NKK - 1]);
           }
-          if (gi < NSM) pieces(xc, NKB - 1, gi, NSM);
+          if constexpr (n < NSM)
+            pieces(ic<n>{}, ic<NSM>{}, [&](auto pc) { softmax_piece(xc, NKB - 1, pc, with_masks); });
         });
   }
 
