@@ -133,10 +133,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   constexpr uint32_t kDscMinusL2 = kTiles * kBQ * 4;     // sm.dsc[b] - sm.l2[b]
   __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
 
-  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-  if (blk >= total) return;
-  const int bh = blk / n_kvblk;
-  const int kvb = blk - bh * n_kvblk;
+  int bh, kvb;
+  if (CAUSAL) {
+    if ((int)blockIdx.x >= total) return;
+    longest_first(blockIdx.x, total / n_kvblk, kvb, bh);  // key block 0 sees every query row
+  } else {
+    const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+    if (blk >= total) return;
+    bh = blk / n_kvblk;
+    kvb = blk - bh * n_kvblk;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;

@@ -84,11 +84,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   constexpr uint32_t kVMinusK = kTiles * kTileBytes;  // sm.v[b] - sm.k[b]
   __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
-  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-  if (blk >= total) return;
-  const int bh = blk / n_qblk;
-  int qblk = blk - bh * n_qblk;
-  if (CAUSAL) qblk = n_qblk - 1 - qblk;  // longest rows first
+  int bh, qblk;
+  if (CAUSAL) {
+    if ((int)blockIdx.x >= total) return;
+    longest_first(blockIdx.x, total / n_qblk, qblk, bh);
+    qblk = n_qblk - 1 - qblk;  // the last query block sees every key
+  } else {
+    const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+    if (blk >= total) return;
+    bh = blk / n_qblk;
+    qblk = blk - bh * n_qblk;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, col = lane & 31;

@@ -136,4 +136,16 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int grid) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+// Causal work items come in ranks of different length (the key range of a
+// query block, the query range of a key block), one item per head and rank.
+// Taking ids rank-major with the longest rank first -- id = rank * BH + head
+// -- and letting the hardware deal consecutive ids to the eight XCDs in turn
+// gives every XCD the same mix of lengths, queued longest first, which keeps
+// the tail of the launch short; when BH is a multiple of 8 all items of one
+// head still run on one XCD.  ids from BH * ranks on do nothing.
+__device__ __forceinline__ void longest_first(int bid, int BH, int& rank, int& head) {
+  rank = bid / BH;
+  head = bid - rank * BH;
+}
+
 }  // namespace fa

@@ -198,11 +198,17 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   constexpr int NDB = DV / 32;   // 32-row blocks of O^T
   __shared__ __attribute__((aligned(16))) FwdSmem<D, DV, SPLIT> sm;
 
-  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
-  if (blk >= total) return;
   const int per_head = n_qblk * n_ksplit;
-  const int bh = blk / per_head;
-  const int rem = blk - bh * per_head;
+  int bh, rem;
+  if (CAUSAL) {
+    if ((int)blockIdx.x >= total) return;
+    longest_first(blockIdx.x, total / per_head, rem, bh);
+  } else {
+    const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+    if (blk >= total) return;
+    bh = blk / per_head;
+    rem = blk - bh * per_head;
+  }
   int qb = rem / n_ksplit;
   const int ks = rem - qb * n_ksplit;
   if (CAUSAL) qb = n_qblk - 1 - qb;  // longest rows first
