@@ -32,6 +32,13 @@ Functions and what pins each one (tests/test_oracle.py):
   streaming_logsumexp the one-pass (max, sum) reduction with its two guards.
                       Pinned by the four-number example and the seeded
                       1000-value example printed on the first page.
+  dropout (module)    dropout whose mask the backward regenerates from the
+                      generator state ("Backward can recreate tiles", second
+                      page): Philox4x32-10 pinned by its published
+                      known-answer vectors; mask layout pinned element by
+                      element; keep rate, p = 0, the expectation of the
+                      output, finite differences and the D identity pin the
+                      forward and backward (tests/test_oracle_dropout.py).
 """
 
 from .attention import (
@@ -43,6 +50,7 @@ from .attention import (
     streaming_logsumexp,
     online_normalizer_trace,
 )
+from . import dropout
 
 __all__ = [
     "attention_forward",
@@ -52,4 +60,5 @@ __all__ = [
     "tiled_forward",
     "streaming_logsumexp",
     "online_normalizer_trace",
+    "dropout",
 ]
