@@ -63,6 +63,11 @@ def library():
         lib.fa_bwd_dkdv.restype = i
         lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd_dq.restype = i
+        u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+        lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, f, u64, u32, vp]
+        lib.fa_fwd_dropout.restype = i
+        lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, f, u64, u32, vp]
+        lib.fa_bwd_dropout.restype = i
         lib.fa_status_string.argtypes = [i]
         lib.fa_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -236,6 +241,54 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
                           _ptr(workspace), B, H, N, d, _scale(scale, d), int(bool(causal)), _stream(q.device))
     if st != FA_OK:
         raise FAError("fa_bwd", st)
+    return dq, dk, dv
+
+
+def _dropout_args(p, seed, offset):
+    p = float(p)
+    if not (0.0 <= p < 1.0):
+        raise ValueError("dropout probability must be in [0, 1)")
+    seed, offset = int(seed), int(offset)
+    if not (0 <= seed < 2 ** 64) or not (0 <= offset < 2 ** 32):
+        raise ValueError("seed must fit 64 bits and offset 32 bits (unsigned)")
+    return p, seed, offset
+
+
+def forward_dropout(q, k, v, p, seed, offset=0, causal=False, scale=None, out=None, lse=None):
+    """forward() with dropout on the normalised weights (fa_fwd_dropout).
+
+    The mask is a function of (seed, offset, head, row, key) only, so
+    backward_dropout with the same arguments regenerates it.  bf16 inputs of
+    one shared [B,H,N,d] shape; L is the logsumexp without dropout.
+    """
+    if q.dtype != torch.bfloat16:
+        raise TypeError("dropout takes bfloat16 Q, K, V")
+    p, seed, offset = _dropout_args(p, seed, offset)
+    _check(q, k, v)
+    B, H, N, d = q.shape
+    o, l = _outputs(q, v, out, lse)
+    st = library().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d, _scale(scale, d),
+                                  int(bool(causal)), p, seed, offset, _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_fwd_dropout", st)
+    return o, l
+
+
+def backward_dropout(q, k, v, o, lse, do, p, seed, offset=0, causal=False, scale=None, workspace=None):
+    """Gradients of sum(dO * O) for O = forward_dropout(q, k, v, p, seed,
+    offset, causal, scale) (fa_bwd_dropout); the mask is regenerated."""
+    _check_bwd(q, k, v, o, lse, do)
+    p, seed, offset = _dropout_args(p, seed, offset)
+    B, H, N, d = q.shape
+    workspace = workspace_for(q, workspace)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    st = library().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(workspace), B, H, N, d, _scale(scale, d), int(bool(causal)), p, seed,
+                                  offset, _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_bwd_dropout", st)
     return dq, dk, dv
 
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace {
@@ -49,6 +50,23 @@ int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.f) ? FA
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Dropout parameters for probability p: keep iff the generator byte >= t,
+// t = min(255, round(256 p)); kept weights are scaled by 256 / (256 - t).
+// Returns FA_ERR_DROPOUT unless 0 <= p < 1; *active is false when t = 0
+// (nothing is dropped, the plain kernels run).
+int make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* out, bool* active) {
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return FA_ERR_DROPOUT;
+  int t = (int)std::floor(256.0 * (double)p + 0.5);
+  if (t > 255) t = 255;
+  out->k0 = (uint32_t)(seed & 0xffffffffu);
+  out->k1 = (uint32_t)(seed >> 32);
+  out->offset = offset;
+  out->t = t;
+  out->r = (float)(256.0 / (256 - t));
+  *active = t > 0;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -61,7 +79,22 @@ int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, in
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, scale, stream));
+  return hip_status(
+      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, scale, nullptr, stream));
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream) {
+  bool empty = false, active = false;
+  fa::Dropout dp{};
+  int st = check_shape(B, H, N, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if ((st = make_dropout(p_drop, seed, offset, &dp, &active)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, scale,
+                                        active ? &dp : nullptr, stream));
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int Nq, int Nk, int d,
@@ -72,7 +105,8 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (empty) return FA_OK;
   if (!o || !lse || (Nk > 0 && (!q || !k || !v))) return FA_ERR_NULL;
-  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, scale, stream));
+  return hip_status(
+      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, scale, nullptr, stream));
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dv, int n_splits) {
@@ -96,7 +130,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float*
   const int n = fa::fwd_splitkv_resolve(B * H, Nq, Nk, d, dv, n_splits);
   if (n > 1 && !workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, n,
-                                        static_cast<float*>(workspace), scale, stream));
+                                        static_cast<float*>(workspace), scale, nullptr, stream));
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
@@ -127,7 +161,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const fl
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (!workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
-                                        N, d, scale, causal, stream));
+                                        N, d, scale, causal, nullptr, stream));
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                   float* dq, float* dk, float* dv, void* workspace, int B, int H, int N, int d, float scale,
+                   int causal, float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream) {
+  bool empty = false, active = false;
+  fa::Dropout dp{};
+  int st = check_shape(B, H, N, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if ((st = make_dropout(p_drop, seed, offset, &dp, &active)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!workspace) return FA_ERR_WORKSPACE;
+  return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
+                                        N, d, scale, causal, active ? &dp : nullptr, stream));
 }
 
 int fa_bwd_prep(const void* dout, const float* o, const float* lse, void* workspace, int B, int H, int N, int d,
@@ -152,7 +202,7 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
   if (!q || !k || !v || !dout || !dk || !dv) return FA_ERR_NULL;
   if (!workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_bwd_dkdv(q, k, v, dout, static_cast<const float*>(workspace), dk, dv, B * H, N, d,
-                                        scale, causal, stream));
+                                        scale, causal, nullptr, stream));
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const void* workspace, float* dq,
@@ -166,7 +216,8 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
   if (!workspace) return FA_ERR_WORKSPACE;
   const float* ws = static_cast<const float*>(workspace);
   const size_t rows = (size_t)B * (size_t)H * (size_t)N;
-  return hip_status(fa::launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, B * H, N, d, scale, causal, stream));
+  return hip_status(
+      fa::launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, B * H, N, d, scale, causal, nullptr, stream));
 }
 
 const char* fa_status_string(int status) {
@@ -178,6 +229,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_WORKSPACE: return "workspace is NULL";
     case FA_ERR_HIP: return "HIP runtime rejected a kernel launch";
+    case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1)";
     default: return "unknown fa_status";
   }
 }

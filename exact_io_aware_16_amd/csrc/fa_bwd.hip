@@ -42,6 +42,7 @@
 //  LDS address is a lane constant XOR a compile-time mask, plus an
 //  immediate.
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 #include "fa_lds.h"
 
@@ -120,11 +121,12 @@ struct QCopy {
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     const bf16_raw* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dsc,
-    float* __restrict__ dK, float* __restrict__ dV, int N, int n_kvblk, int total, float scale, float c) {
+    float* __restrict__ dK, float* __restrict__ dV, int N, int n_kvblk, int total, float scale, float c,
+    Dropout drop) {
   constexpr int NKK = D / 16;  // 16-wide head-dim slices (contraction of S and dP)
   constexpr int NDB = D / 32;  // 32-row blocks of dK^T / dV^T
   constexpr int RB = D * 2;    // bytes per Q / dO / K row
@@ -305,6 +307,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // take the code without masks.
   float lvd[2][16], pv[8], dv8[8];
   int dead = 0;
+  uint32_t dm[4] = {0u, 0u, 0u, 0u};           // dropout mask words of the current block
+  const float scale_r = DROP ? scale * drop.r : scale;
   // L log2 e and scale D of chunk h of block qb of step x into lvd[h]
   auto load_ld = [&](const Step& x, int qb, auto hc) {
     constexpr int h = decltype(hc)::value;
@@ -326,6 +330,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   auto softmax_piece = [&](const Step& x, int qb, auto pc, auto masked, const Step& xn, int qbn, bool has_next) {
     constexpr int piece = decltype(pc)::value, h = piece >> 2, e0 = 2 * (piece & 3);
     constexpr bool M = decltype(masked)::value;
+    if constexpr (DROP && piece == 0) {
+      // dropout mask of this 32-row block: lane q of each 4-lane group
+      // computes the 4 x 4 block of rows 16 (q / 2) + 8 g + 4 (q % 2) .. + 3
+      // and the group's keys; after the byte and word exchange dm[x] holds
+      // this key's column of block x, row r in byte r
+      const int qd = col & 3;
+      uint32_t w[4] = {(uint32_t)my_key >> 2,
+                       (uint32_t)(x.q0 + 32 * qb + 16 * (qd >> 1) + 8 * g + 4 * (qd & 1)) >> 2, (uint32_t)bh,
+                       drop.offset};
+      philox4x32_10(w, drop.k0, drop.k1);
+      uint32_t cols[4];
+      byte_transpose(w, cols);
+      quad_transpose(cols, dm, qd);
+    }
     if constexpr ((piece & 3) == 0) {
       if constexpr (h == 0) load_ld(x, qb, ic<1>{});
       else if (has_next) load_ld(xn, qbn, ic<0>{});
@@ -340,8 +358,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     for (int e = e0; e < e0 + 2; ++e) {
       float pe = fast_exp2(fmaf(s[qb][8 * h + e], c, -lvd[h][e]));
       if constexpr (M) pe = e < dead ? 0.f : pe;
-      pv[e] = pe;
-      dv8[e] = pe * fmaf(dp[qb][8 * h + e], scale, -lvd[h][8 + e]);
+      if constexpr (DROP) {
+        // a dropped pair adds nothing to dV and its dP term vanishes from dS'
+        const bool keep = kept(dm[2 * h + (e >> 2)], e & 3, drop.t);
+        pv[e] = keep ? pe : 0.f;
+        dv8[e] = pe * fmaf(dp[qb][8 * h + e], keep ? scale_r : 0.f, -lvd[h][8 + e]);
+      } else {
+        pv[e] = pe;
+        dv8[e] = pe * fmaf(dp[qb][8 * h + e], scale, -lvd[h][8 + e]);
+      }
     }
     if constexpr ((piece & 3) == 3) {
       pb[qb][h] = pack_bf16x8(pv);
@@ -481,8 +506,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const int d = 32 * db + 8 * i4 + 4 * g;
         *reinterpret_cast<float4*>(dKrow + d) =
             make_float4(dk_acc[db][4 * i4], dk_acc[db][4 * i4 + 1], dk_acc[db][4 * i4 + 2], dk_acc[db][4 * i4 + 3]);
-        *reinterpret_cast<float4*>(dVrow + d) =
-            make_float4(dv_acc[db][4 * i4], dv_acc[db][4 * i4 + 1], dv_acc[db][4 * i4 + 2], dv_acc[db][4 * i4 + 3]);
+        const float rv = DROP ? drop.r : 1.f;  // kept weights carry the factor 256 / (256 - t)
+        *reinterpret_cast<float4*>(dVrow + d) = make_float4(rv * dv_acc[db][4 * i4], rv * dv_acc[db][4 * i4 + 1],
+                                                            rv * dv_acc[db][4 * i4 + 2], rv * dv_acc[db][4 * i4 + 3]);
       }
   }
 }
@@ -499,18 +525,18 @@ hipError_t launch_prep(const void* dout, const float* o, const float* lse, float
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws, float* dk,
-                       float* dv, int BH, int N, float scale, hipStream_t stream) {
+                       float* dv, int BH, int N, float scale, const Dropout& drop, hipStream_t stream) {
   const long long rows = (long long)BH * N;
   const int n_kvblk = (N + kBKV - 1) / kBKV;
   const long long total = (long long)BH * n_kvblk;
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROP>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k), static_cast<const bf16_raw*>(v),
                      static_cast<const bf16_raw*>(dout), ws + rows, ws, dk, dv, N, n_kvblk, (int)total, scale,
-                     scale * kLog2e);
+                     scale * kLog2e, drop);
   return hipGetLastError();
 }
 
@@ -522,23 +548,32 @@ hipError_t launch_bwd_prep(const void* dout, const float* o, const float* lse, f
                   : launch_prep<64>(dout, o, lse, ws, BH, N, scale, stream);
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv_drop(const void* q, const void* k, const void* v, const void* dout, const float* ws,
+                            float* dk, float* dv, int BH, int N, float scale, const Dropout* drop,
+                            hipStream_t stream) {
+  if (drop) return launch_dkdv<D, CAUSAL, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, *drop, stream);
+  return launch_dkdv<D, CAUSAL, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, Dropout{}, stream);
+}
+
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws,
-                           float* dk, float* dv, int BH, int N, int d, float scale, int causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch_dkdv<128, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, stream)
-                              : launch_dkdv<128, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, stream);
-  return causal ? launch_dkdv<64, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, stream)
-                : launch_dkdv<64, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, stream);
+                           float* dk, float* dv, int BH, int N, int d, float scale, int causal, const Dropout* drop,
+                           hipStream_t stream) {
+  if (d == 128) return causal ? launch_dkdv_drop<128, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, stream)
+                              : launch_dkdv_drop<128, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, stream);
+  return causal ? launch_dkdv_drop<64, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, stream)
+                : launch_dkdv_drop<64, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* ws, int BH, int N, int d,
-                           float scale, int causal, hipStream_t stream) {
+                           float scale, int causal, const Dropout* drop, hipStream_t stream) {
   hipError_t e = launch_bwd_prep(dout, o, lse, ws, BH, N, d, scale, stream);
   if (e != hipSuccess) return e;
-  e = launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, N, d, scale, causal, stream);
+  e = launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, N, d, scale, causal, drop, stream);
   if (e != hipSuccess) return e;
   const long long rows = (long long)BH * N;
-  return launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, BH, N, d, scale, causal, stream);
+  return launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, BH, N, d, scale, causal, drop, stream);
 }
 
 }  // namespace fa

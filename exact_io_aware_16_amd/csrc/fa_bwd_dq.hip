@@ -22,6 +22,7 @@
 //  * causal: query block qb visits key tiles up to its diagonal only, masks
 //    are applied only on tiles that straddle the diagonal or the ragged end.
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 #include "fa_lds.h"
 
@@ -70,11 +71,11 @@ struct KvCopy {
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     const bf16_raw* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dsc,
-    float* __restrict__ dQ, int N, int n_qblk, int total, float scale, float c) {
+    float* __restrict__ dQ, int N, int n_qblk, int total, float scale, float c, Dropout drop) {
   constexpr int BC = DqTile<D>::BC;
   constexpr int NKB = BC / 32;  // 32-key blocks per tile
   constexpr int NKK = D / 16;   // 16-wide head-dim slices (contraction of S and dP)
@@ -241,8 +242,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   // compile-time flag: tiles below the diagonal and inside the sequence take
   // the code without masks.
   float dsv[8];
+  uint32_t dm[4] = {0u, 0u, 0u, 0u};  // dropout mask words of the current block
+  const float scale_r = DROP ? scale * drop.r : scale;
   auto softmax_piece = [&](const Tile& x, int kb, auto pc, auto masked) {
     constexpr int piece = decltype(pc)::value, h = piece >> 2, e0 = 2 * (piece & 3);
+    if constexpr (DROP && piece == 0) {
+      // dropout mask of this 32-key block: lane q of each 4-lane group
+      // computes the 4 x 4 block of the group's rows and keys
+      // 16 (q / 2) + 8 g + 4 (q % 2) .. + 3; after the word exchange dm[x]
+      // holds this row's word of block x
+      const int qd = col & 3;
+      uint32_t w[4] = {(uint32_t)(x.key0 + 32 * kb + 16 * (qd >> 1) + 8 * g + 4 * (qd & 1)) >> 2,
+                       (uint32_t)my_q >> 2, (uint32_t)bh, drop.offset};
+      philox4x32_10(w, drop.k0, drop.k1);
+      quad_transpose(w, dm, qd);
+    }
     // register 8 h + e of half g holds key key0 + 32 kb + 16 h + 8 g + e
     int lim = 0;
     if constexpr (decltype(masked)::value) lim = last_key - (x.key0 + 32 * kb + 16 * h + 8 * g);
@@ -250,7 +264,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     for (int e = e0; e < e0 + 2; ++e) {
       float pe = fast_exp2(fmaf(st[kb][8 * h + e], c, -l2q));
       if constexpr (decltype(masked)::value) pe = e > lim ? 0.f : pe;
-      dsv[e] = pe * fmaf(dpt[kb][8 * h + e], scale, -dq_sc);
+      if constexpr (DROP)  // a dropped pair's dP term vanishes from dS'
+        dsv[e] = pe * fmaf(dpt[kb][8 * h + e], kept(dm[2 * h + (e >> 2)], e & 3, drop.t) ? scale_r : 0.f, -dq_sc);
+      else
+        dsv[e] = pe * fmaf(dpt[kb][8 * h + e], scale, -dq_sc);
     }
     if constexpr ((piece & 3) == 3) dsb[kb][h] = pack_bf16x8(dsv);
   };
@@ -389,28 +406,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t launch(const void* q, const void* k, const void* v, const void* dout, const float* l2, const float* dsc,
-                  float* dq, int BH, int N, float scale, hipStream_t stream) {
+                  float* dq, int BH, int N, float scale, const Dropout& drop, hipStream_t stream) {
   const int n_qblk = (N + kBR - 1) / kBR;
   const long long total = (long long)BH * n_qblk;
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k), static_cast<const bf16_raw*>(v),
-                     static_cast<const bf16_raw*>(dout), l2, dsc, dq, N, n_qblk, (int)total, scale, scale * kLog2e);
+                     static_cast<const bf16_raw*>(dout), l2, dsc, dq, N, n_qblk, (int)total, scale, scale * kLog2e,
+                     drop);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_drop(const void* q, const void* k, const void* v, const void* dout, const float* l2,
+                       const float* dsc, float* dq, int BH, int N, float scale, const Dropout* drop,
+                       hipStream_t stream) {
+  if (drop) return launch<D, CAUSAL, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, *drop, stream);
+  return launch<D, CAUSAL, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, Dropout{}, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
                               const float* dsc, float* dq, int BH, int N, int d, float scale, int causal,
-                              hipStream_t stream) {
-  if (d == 128) return causal ? launch<128, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, stream)
-                              : launch<128, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, stream);
-  return causal ? launch<64, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, stream)
-                : launch<64, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, stream);
+                              const Dropout* drop, hipStream_t stream) {
+  if (d == 128) return causal ? launch_drop<128, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, stream)
+                              : launch_drop<128, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, stream);
+  return causal ? launch_drop<64, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, stream)
+                : launch_drop<64, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, stream);
 }
 
 }  // namespace fa

@@ -45,6 +45,7 @@
 #include <algorithm>
 
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -187,11 +188,11 @@ __device__ __forceinline__ void tile_scores(f32x16 (&s)[BC / 32], const char* kt
 // tiles_per_split tiles; workgroup (head, query block, range ks) writes the
 // range's own normalised output and logsumexp to O + ks * BH*Nq*DV and
 // LSE + ks * BH*Nq, and splitkv_merge_kernel combines the ranges.
-template <int D, int DV, bool CAUSAL, int SPLIT>
+template <int D, int DV, bool CAUSAL, int SPLIT, bool DROP>
 __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk, int n_qblk, int n_ksplit,
-    int tiles_per_split, int total, float c) {
+    int tiles_per_split, int total, float c, Dropout dp) {
   constexpr int BC = FwdTile<D, DV>::BC;
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NKK = D / 16;    // 16-wide slices of the head dimension
@@ -348,7 +349,18 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;  // row with nothing visible yet
 
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      // dropout mask words of this 32-key block: dm[x] is this row's word of
+      // the 4 x 4 block holding keys 16 (x / 2) + 8 g + 4 (x % 2) .. + 3 (lane
+      // x of the 4-lane group computes that block)
+      uint32_t dm[4];
+      if constexpr (DROP) {
+        const int qd = col & 3;
+        uint32_t w[4] = {(uint32_t)(key0 + 32 * kb + 16 * (qd >> 1) + 8 * g + 4 * (qd & 1)) >> 2,
+                         (uint32_t)my_q >> 2, (uint32_t)bh, dp.offset};
+        philox4x32_10(w, dp.k0, dp.k1);
+        quad_transpose(w, dm, qd);
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         float p[8];
@@ -360,9 +372,13 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
         pb[kb][h] = pack_bf16x8(p);
         // l_rnd sums the bf16-rounded weights that actually multiply V, so O
         // is normalised by exactly the weights applied (a dominant weight's
-        // rounding cancels in O / l_rnd); l_run (exact terms) gives L.
+        // rounding cancels in O / l_rnd); l_run (exact terms) gives L.  With
+        // dropout both sums cover every weight; only the product with V
+        // loses the dropped ones.
         l_rnd = sum_bf16x8(pb[kb][h], l_rnd);
+        if constexpr (DROP) pb[kb][h] = drop_bf16x8(pb[kb][h], dm[2 * h], dm[2 * h + 1], dp.t);
       }
+    }
 
     // O^T += V^T P^T, V^T operand via transpose reads of the row-major tile;
     // operand sets rotate per (key block, half) group
@@ -427,7 +443,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   const float l_tot = halves_sum(l_run);
   const float l_nrm = halves_sum(l_rnd);
   if (my_q < Nq) {
-    const float inv = l_nrm > 0.f ? 1.f / l_nrm : 0.f;
+    const float inv = l_nrm > 0.f ? (DROP ? dp.r : 1.f) / l_nrm : 0.f;
     float* Orow = O + ((size_t)ks * BH + bh) * Nq * DV + (size_t)my_q * DV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -478,9 +494,9 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restr
   if (part == 0) LSE[row] = den > 0.f ? m + __logf(den) : -INFINITY;
 }
 
-template <int D, int DV, bool CAUSAL>
+template <int D, int DV, bool CAUSAL, bool DROP>
 hipError_t launch(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
-                  int n_ksplit, float* ws, float scale, hipStream_t stream) {
+                  int n_ksplit, float* ws, float scale, const Dropout& dp, hipStream_t stream) {
   constexpr int BC = FwdTile<D, DV>::BC;
   const int n_qblk = (Nq + kBR - 1) / kBR;
   const int n_ktiles = (Nk + BC - 1) / BC;
@@ -497,15 +513,15 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
   // workgroup's key tiles over 8 waves instead.
   const bool split = total < 2 * kComputeUnits && (n_ktiles + n_ksplit - 1) / n_ksplit > 1;
   if (split)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 2>), dim3(grid), dim3(2 * kThreads), 0, stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 2, DROP>), dim3(grid), dim3(2 * kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
                        static_cast<const bf16_raw*>(v), o_dst, l_dst, BH, Nq, Nk, n_qblk, n_ksplit, tiles_per_split,
-                       (int)total, scale * kLog2e);
+                       (int)total, scale * kLog2e, dp);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 1>), dim3(grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 1, DROP>), dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
                        static_cast<const bf16_raw*>(v), o_dst, l_dst, BH, Nq, Nk, n_qblk, n_ksplit, tiles_per_split,
-                       (int)total, scale * kLog2e);
+                       (int)total, scale * kLog2e, dp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_ksplit == 1) return e;
   const long long rows = (long long)BH * Nq;
@@ -519,9 +535,15 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
 
 template <int D, bool CAUSAL>
 hipError_t launch_dv(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
-                     int dv, int n_ksplit, float* ws, float scale, hipStream_t stream) {
-  return dv == 128 ? launch<D, 128, CAUSAL>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, stream)
-                   : launch<D, 64, CAUSAL>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, stream);
+                     int dv, int n_ksplit, float* ws, float scale, const Dropout* drop, hipStream_t stream) {
+  // dropout is offered for the square contract (dv = d) only
+  if (drop) {
+    if (dv != D) return hipErrorInvalidValue;
+    return launch<D, D, CAUSAL, true>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, *drop, stream);
+  }
+  const Dropout none{};
+  return dv == 128 ? launch<D, 128, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, stream)
+                   : launch<D, 64, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, stream);
 }
 
 }  // namespace
@@ -544,11 +566,12 @@ int fwd_splitkv_resolve(int BH, int Nq, int Nk, int d, int dv, int n_splits) {
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq,
                            int Nk, int d, int dv, int causal, int n_ksplit, float* ws, float scale,
-                           hipStream_t stream) {
-  if (d == 128) return causal ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, stream)
-                              : launch_dv<128, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, stream);
-  return causal ? launch_dv<64, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, stream)
-                : launch_dv<64, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, stream);
+                           const Dropout* drop, hipStream_t stream) {
+  if (d == 128)
+    return causal ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, stream)
+                  : launch_dv<128, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, stream);
+  return causal ? launch_dv<64, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, stream)
+                : launch_dv<64, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, stream);
 }
 
 }  // namespace fa

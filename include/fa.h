@@ -39,6 +39,7 @@
 #define FA_H
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -54,7 +55,8 @@ typedef enum {
   FA_ERR_HEADDIM = 3,   /* d is not a supported head width (64 or 128)         */
   FA_ERR_SCALE = 4,     /* scale is not finite and > 0                         */
   FA_ERR_WORKSPACE = 5, /* a required workspace is NULL                        */
-  FA_ERR_HIP = 6        /* a kernel launch was rejected by the HIP runtime     */
+  FA_ERR_HIP = 6,       /* a kernel launch was rejected by the HIP runtime     */
+  FA_ERR_DROPOUT = 7    /* dropout probability not in [0, 1)                   */
 } fa_status;
 
 /*
@@ -137,6 +139,32 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 int fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
            const void* dout, float* dq, float* dk, float* dv, void* workspace,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Attention dropout whose mask the backward regenerates from the generator
+ * state instead of storing it ("Backward can recreate tiles instead of
+ * retaining the square", Why FlashAttention Can Avoid a Square Attention
+ * Array Without Making Attention Linear).  Same arguments, layouts,
+ * ownership and errors as fa_fwd / fa_bwd, plus:
+ *   p_drop : dropout probability, 0 <= p_drop < 1, else FA_ERR_DROPOUT
+ *   seed   : 64-bit generator key;  offset : 32-bit stream selector
+ * Mask: for head bh = b*H + h, query row i, key j, the Philox4x32-10
+ * generator (Salmon et al., SC 2011) with counter (j/4, i/4, bh, offset)
+ * and key (seed mod 2^32, seed / 2^32) gives four words; the pair is kept
+ * iff byte (j mod 4) of word (i mod 4) is >= t = min(255, round(256 p_drop)),
+ * and kept weights are multiplied by 256 / (256 - t).  The softmax
+ * normaliser and lse cover every weight (dropout acts on the normalised
+ * probabilities): O = (P * keep * 256/(256-t)) V.  fa_bwd_dropout with the
+ * same p_drop, seed and offset gives the gradients of that O; the workspace
+ * is fa_bwd_workspace_bytes.  p_drop = 0 runs the plain kernels.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                   const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream);
 
 /*
  * The three phases fa_bwd runs, for callers that schedule or time them
