@@ -12,6 +12,8 @@ Also reported on the same line:
   fwd        forward alone on B=1, H=8, N=4096, d=128, non-causal
   decode     split-KV forward (fa_fwd_splitkv), one query row per head against
              32768 keys, B=1, H=32, d=dv=128, against the HBM roofline
+  dropout    the step's forward and backward with dropout p = 0.1
+             (fa_fwd_dropout + fa_bwd_dropout, mask regenerated from the seed)
   phases     forward and backward of the step timed separately
   kernels    each kernel of the step timed alone through its C entry point
              (fa_fwd, fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq)
@@ -220,6 +222,19 @@ def main():
                  + bh * dc["Nq"] * (dc["dv"] + 1) * 4)
     dec_gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
 
+    # ------------------------------------------------------------ the step with dropout
+    def step_drop():
+        fa.forward_dropout(q, k, v, 0.1, 2024, 0, causal=True, out=o, lse=lse)
+        fa.backward_dropout(q, k, v, o, lse, do, 0.1, 2024, 0, causal=True, workspace=ws)
+
+    def fwd_drop():
+        fa.forward_dropout(q, k, v, 0.1, 2024, 0, causal=True, out=o, lse=lse)
+
+    for _ in range(3):
+        step_drop()
+    ms_drop = time_calls(step_drop, args.steps, stream)
+    ms_drop_fwd = time_calls(fwd_drop, args.steps, stream)
+
     res = {
         "metric": "attention TFLOP/s (fwd, fwd+bwd) bf16 at 1 MI355X; % of MFMA peak",
         "value": round(value, 2),
@@ -288,6 +303,14 @@ def main():
                 "traffic": None,
                 "algorithmic_bytes_per_call": dec_bytes,
             },
+        },
+        "dropout": {
+            "workload": w.name + "_dropout0.1",
+            "step_ms": round(ms_drop, 4),
+            "step_tflops": round(step_flop / (ms_drop * 1e-3) / 1e12, 2),
+            "fwd_ms": round(ms_drop_fwd, 4),
+            "fwd_tflops": round(w.fwd_flop() / (ms_drop_fwd * 1e-3) / 1e12, 2),
+            "flop_convention": "same FLOP as the step without dropout",
         },
         "timed_wall_s": round(wall, 3),
     }
