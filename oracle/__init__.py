@@ -39,6 +39,10 @@ Functions and what pins each one (tests/test_oracle.py):
                       element; keep rate, p = 0, the expectation of the
                       output, finite differences and the D identity pin the
                       forward and backward (tests/test_oracle_dropout.py).
+  varlen (module)     packed variable-length sequences ("Padding is silent
+                      waste", first page): per-sequence plain attention,
+                      pinned against one masked softmax over the whole packed
+                      axis and its torch autograd (tests/test_oracle_varlen.py).
 """
 
 from .attention import (
@@ -50,7 +54,7 @@ from .attention import (
     streaming_logsumexp,
     online_normalizer_trace,
 )
-from . import dropout
+from . import dropout, varlen
 
 __all__ = [
     "attention_forward",
@@ -61,4 +65,5 @@ __all__ = [
     "streaming_logsumexp",
     "online_normalizer_trace",
     "dropout",
+    "varlen",
 ]
