@@ -68,6 +68,10 @@ def library():
         lib.fa_fwd_dropout.restype = i
         lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, f, u64, u32, vp]
         lib.fa_bwd_dropout.restype = i
+        lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        lib.fa_fwd_varlen.restype = i
+        lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        lib.fa_bwd_varlen.restype = i
         lib.fa_status_string.argtypes = [i]
         lib.fa_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -289,6 +293,75 @@ def backward_dropout(q, k, v, o, lse, do, p, seed, offset=0, causal=False, scale
                                   offset, _stream(q.device))
     if st != FA_OK:
         raise FAError("fa_bwd_dropout", st)
+    return dq, dk, dv
+
+
+def _check_varlen(q, k, v, cu_seqlens, max_seqlen):
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("packed sequences take bfloat16 Q, K, V")
+        if t.dim() != 3:
+            raise ValueError("packed Q, K, V must be rank 3 [H, total, d]")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("packed Q, K and V must have one shape [H, total, d]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor of B + 1 offsets")
+    if not all(t.is_contiguous() for t in (q, k, v, cu_seqlens)):
+        raise ValueError("packed tensors and cu_seqlens must be contiguous")
+    if not (q.device == k.device == v.device == cu_seqlens.device) or q.device.type != "cuda":
+        raise ValueError("packed tensors and cu_seqlens must be on one GPU")
+    max_seqlen = int(max_seqlen)
+    if max_seqlen < 0 or max_seqlen > q.shape[1]:
+        raise ValueError("max_seqlen must be in [0, total]")
+    return max_seqlen
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out=None, lse=None):
+    """Attention over packed variable-length sequences (fa_fwd_varlen).
+
+    q, k, v: bf16 [H, total, d]; sequence b holds rows cu_seqlens[b] ..
+    cu_seqlens[b+1]-1 of every head (cu_seqlens: int32 [B+1] on the GPU);
+    max_seqlen bounds the longest sequence.  Returns O float32 [H, total, d]
+    and L float32 [H, total]; rows attend within their own sequence.
+    """
+    max_seqlen = _check_varlen(q, k, v, cu_seqlens, max_seqlen)
+    H, total, d = q.shape
+    B = cu_seqlens.numel() - 1
+    o = out if out is not None else torch.empty((H, total, d), dtype=torch.float32, device=q.device)
+    l = lse if lse is not None else torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if o.shape != (H, total, d) or l.shape != (H, total) or o.dtype != torch.float32 or l.dtype != torch.float32:
+        raise ValueError("out must be float32 [H, total, d] and lse float32 [H, total]")
+    st = library().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _ptr(cu_seqlens), B, H, total,
+                                 max_seqlen, d, _scale(scale, d), int(bool(causal)), _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_fwd_varlen", st)
+    return o, l
+
+
+def backward_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, scale=None, workspace=None):
+    """Gradients (dQ, dK, dV), float32 [H, total, d], of sum(dO * O) for
+    O = forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal, scale)
+    (fa_bwd_varlen)."""
+    max_seqlen = _check_varlen(q, k, v, cu_seqlens, max_seqlen)
+    H, total, d = q.shape
+    B = cu_seqlens.numel() - 1
+    if do.dtype != torch.bfloat16 or do.shape != q.shape or not do.is_contiguous():
+        raise ValueError("dO must be a contiguous bfloat16 tensor of Q's shape")
+    if o.dtype != torch.float32 or o.shape != q.shape or lse.dtype != torch.float32 or lse.shape != (H, total):
+        raise ValueError("O and L must be the float32 outputs of forward_varlen")
+    ws_bytes = library().fa_bwd_workspace_bytes(1, H, total, d)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace too small: need {ws_bytes} bytes")
+    dq = torch.empty((H, total, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    st = library().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(workspace), _ptr(cu_seqlens), B, H, total, max_seqlen, d,
+                                 _scale(scale, d), int(bool(causal)), _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_bwd_varlen", st)
     return dq, dk, dv
 
 

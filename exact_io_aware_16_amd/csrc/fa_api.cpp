@@ -46,6 +46,20 @@ int check_shape_ex(int B, int H, int Nq, int Nk, int d, int dv, int causal, bool
   return FA_OK;
 }
 
+// Packed sequences: Q, K, V [H, total, d]; cu_seqlens has B + 1 entries.
+int check_varlen(int B, int H, int total, int max_seqlen, int d, int causal, bool* empty) {
+  if (B < 0 || H < 0 || total < 0 || max_seqlen < 0) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  *empty = (B == 0 || H == 0 || total == 0 || max_seqlen == 0);
+  if ((long long)B * H > INT32_MAX) return FA_ERR_SHAPE;
+  if ((double)H * total * d > 4.0e18) return FA_ERR_SHAPE;
+  // a sequence is addressed through buffer descriptors with 32-bit byte
+  // offsets, and none is longer than the packed axis
+  if ((long long)total * d * 4 > INT32_MAX || max_seqlen > total) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
@@ -80,7 +94,7 @@ int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, in
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   return hip_status(
-      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, scale, nullptr, stream));
+      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, scale, nullptr, nullptr, stream));
 }
 
 int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int d,
@@ -94,7 +108,7 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float*
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, scale,
-                                        active ? &dp : nullptr, stream));
+                                        active ? &dp : nullptr, nullptr, stream));
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int Nq, int Nk, int d,
@@ -106,7 +120,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,
   if (empty) return FA_OK;
   if (!o || !lse || (Nk > 0 && (!q || !k || !v))) return FA_ERR_NULL;
   return hip_status(
-      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, scale, nullptr, stream));
+      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, scale, nullptr, nullptr, stream));
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dv, int n_splits) {
@@ -130,7 +144,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float*
   const int n = fa::fwd_splitkv_resolve(B * H, Nq, Nk, d, dv, n_splits);
   if (n > 1 && !workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, n,
-                                        static_cast<float*>(workspace), scale, nullptr, stream));
+                                        static_cast<float*>(workspace), scale, nullptr, nullptr, stream));
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
@@ -161,7 +175,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const fl
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (!workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
-                                        N, d, scale, causal, nullptr, stream));
+                                        N, d, scale, causal, nullptr, nullptr, stream));
 }
 
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
@@ -177,7 +191,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, 
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (!workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
-                                        N, d, scale, causal, active ? &dp : nullptr, stream));
+                                        N, d, scale, causal, active ? &dp : nullptr, nullptr, stream));
 }
 
 int fa_bwd_prep(const void* dout, const float* o, const float* lse, void* workspace, int B, int H, int N, int d,
@@ -202,7 +216,7 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
   if (!q || !k || !v || !dout || !dk || !dv) return FA_ERR_NULL;
   if (!workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_bwd_dkdv(q, k, v, dout, static_cast<const float*>(workspace), dk, dv, B * H, N, d,
-                                        scale, causal, nullptr, stream));
+                                        scale, causal, nullptr, nullptr, stream));
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const void* workspace, float* dq,
@@ -217,7 +231,35 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
   const float* ws = static_cast<const float*>(workspace);
   const size_t rows = (size_t)B * (size_t)H * (size_t)N;
   return hip_status(
-      fa::launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, B * H, N, d, scale, causal, nullptr, stream));
+      fa::launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, B * H, N, d, scale, causal, nullptr, nullptr, stream));
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse, const int* cu_seqlens, int B,
+                  int H, int total, int max_seqlen, int d, float scale, int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_varlen(B, H, total, max_seqlen, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
+  const fa::Seqs sq{cu_seqlens, H, total};
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, max_seqlen, max_seqlen, d, d, causal, 1, nullptr,
+                                        scale, nullptr, &sq, stream));
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                  float* dq, float* dk, float* dv, void* workspace, const int* cu_seqlens, int B, int H, int total,
+                  int max_seqlen, int d, float scale, int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_varlen(B, H, total, max_seqlen, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !cu_seqlens) return FA_ERR_NULL;
+  if (!workspace) return FA_ERR_WORKSPACE;
+  const fa::Seqs sq{cu_seqlens, H, total};
+  return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
+                                        max_seqlen, d, scale, causal, nullptr, &sq, stream));
 }
 
 const char* fa_status_string(int status) {

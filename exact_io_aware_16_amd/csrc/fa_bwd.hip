@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     const bf16_raw* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dsc,
     float* __restrict__ dK, float* __restrict__ dV, int N, int n_kvblk, int total, float scale, float c,
-    Dropout drop) {
+    Dropout drop, Seqs seqs) {
   constexpr int NKK = D / 16;  // 16-wide head-dim slices (contraction of S and dP)
   constexpr int NDB = D / 32;  // 32-row blocks of dK^T / dV^T
   constexpr int RB = D * 2;    // bytes per Q / dO / K row
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
 
   int bh, kvb;
-  if (CAUSAL) {
+  if (CAUSAL || seqs.cu) {
     if ((int)blockIdx.x >= total) return;
     longest_first(blockIdx.x, total / n_kvblk, kvb, bh);  // key block 0 sees every query row
   } else {
@@ -148,7 +148,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
-  const size_t head = (size_t)bh * N * D;
+  // first row of this head; for packed sequences, of sequence b = bh / H in
+  // head h = bh % H (then N is that sequence's length and n_kvblk covers the
+  // longest one)
+  size_t row0 = (size_t)bh * N;
+  if (seqs.cu) {
+    const int b = bh / seqs.H, hh = bh - b * seqs.H;
+    int s0, s1;
+    seq_range(seqs, b, s0, s1);
+    N = s1 - s0;
+    row0 = (size_t)hh * seqs.total + s0;
+    if (kvb * kBKV >= N) return;  // past the end of a shorter sequence
+  }
+  const size_t head = row0 * D;
 
   const int k0 = kvb * kBKV;
   const int my_key = k0 + 32 * wave + col;
@@ -159,9 +171,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const __amdgpu_buffer_rsrc_t grs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head), (short)0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t lrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(L2 + (size_t)bh * N), (short)0, N * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(L2 + row0), (short)0, N * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t drs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(Dsc + (size_t)bh * N), (short)0, N * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Dsc + row0), (short)0, N * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(K + head), (short)0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -525,10 +537,18 @@ hipError_t launch_prep(const void* dout, const float* o, const float* lse, float
   return hipGetLastError();
 }
 
+// BH, N: heads and sequence length; for packed sequences the B * H
+// (sequence, head) units and the longest length, the workspace then holding
+// H * total rows.
+long long workspace_rows(int BH, int N, const Seqs& sq) {
+  return sq.cu ? (long long)sq.H * sq.total : (long long)BH * N;
+}
+
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws, float* dk,
-                       float* dv, int BH, int N, float scale, const Dropout& drop, hipStream_t stream) {
-  const long long rows = (long long)BH * N;
+                       float* dv, int BH, int N, float scale, const Dropout& drop, const Seqs& sq,
+                       hipStream_t stream) {
+  const long long rows = workspace_rows(BH, N, sq);
   const int n_kvblk = (N + kBKV - 1) / kBKV;
   const long long total = (long long)BH * n_kvblk;
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
@@ -536,7 +556,7 @@ hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* 
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROP>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k), static_cast<const bf16_raw*>(v),
                      static_cast<const bf16_raw*>(dout), ws + rows, ws, dk, dv, N, n_kvblk, (int)total, scale,
-                     scale * kLog2e, drop);
+                     scale * kLog2e, drop, sq);
   return hipGetLastError();
 }
 
@@ -550,30 +570,38 @@ hipError_t launch_bwd_prep(const void* dout, const float* o, const float* lse, f
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_drop(const void* q, const void* k, const void* v, const void* dout, const float* ws,
-                            float* dk, float* dv, int BH, int N, float scale, const Dropout* drop,
+                            float* dk, float* dv, int BH, int N, float scale, const Dropout* drop, const Seqs& sq,
                             hipStream_t stream) {
-  if (drop) return launch_dkdv<D, CAUSAL, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, *drop, stream);
-  return launch_dkdv<D, CAUSAL, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, Dropout{}, stream);
+  if (drop) {
+    if (sq.cu) return hipErrorInvalidValue;  // dropout is offered for the dense layout only
+    return launch_dkdv<D, CAUSAL, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, *drop, sq, stream);
+  }
+  return launch_dkdv<D, CAUSAL, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, Dropout{}, sq, stream);
 }
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws,
                            float* dk, float* dv, int BH, int N, int d, float scale, int causal, const Dropout* drop,
-                           hipStream_t stream) {
-  if (d == 128) return causal ? launch_dkdv_drop<128, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, stream)
-                              : launch_dkdv_drop<128, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, stream);
-  return causal ? launch_dkdv_drop<64, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, stream)
-                : launch_dkdv_drop<64, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, stream);
+                           const Seqs* seqs, hipStream_t stream) {
+  const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
+  if (d == 128)
+    return causal ? launch_dkdv_drop<128, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, sq, stream)
+                  : launch_dkdv_drop<128, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, sq, stream);
+  return causal ? launch_dkdv_drop<64, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, sq, stream)
+                : launch_dkdv_drop<64, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, sq, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* ws, int BH, int N, int d,
-                           float scale, int causal, const Dropout* drop, hipStream_t stream) {
-  hipError_t e = launch_bwd_prep(dout, o, lse, ws, BH, N, d, scale, stream);
+                           float scale, int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+  const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
+  const long long rows = workspace_rows(BH, N, sq);
+  // the preprocess is row-wise: all H * total packed rows at once
+  hipError_t e = sq.cu ? launch_bwd_prep(dout, o, lse, ws, sq.H, sq.total, d, scale, stream)
+                       : launch_bwd_prep(dout, o, lse, ws, BH, N, d, scale, stream);
   if (e != hipSuccess) return e;
-  e = launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, N, d, scale, causal, drop, stream);
+  e = launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, N, d, scale, causal, drop, seqs, stream);
   if (e != hipSuccess) return e;
-  const long long rows = (long long)BH * N;
-  return launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, BH, N, d, scale, causal, drop, stream);
+  return launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, BH, N, d, scale, causal, drop, seqs, stream);
 }
 
 }  // namespace fa

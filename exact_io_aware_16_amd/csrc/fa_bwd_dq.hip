@@ -75,7 +75,7 @@ template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     const bf16_raw* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dsc,
-    float* __restrict__ dQ, int N, int n_qblk, int total, float scale, float c, Dropout drop) {
+    float* __restrict__ dQ, int N, int n_qblk, int total, float scale, float c, Dropout drop, Seqs seqs) {
   constexpr int BC = DqTile<D>::BC;
   constexpr int NKB = BC / 32;  // 32-key blocks per tile
   constexpr int NKK = D / 16;   // 16-wide head-dim slices (contraction of S and dP)
@@ -86,10 +86,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
   int bh, qblk;
-  if (CAUSAL) {
+  if (CAUSAL || seqs.cu) {
     if ((int)blockIdx.x >= total) return;
     longest_first(blockIdx.x, total / n_qblk, qblk, bh);
-    qblk = n_qblk - 1 - qblk;  // the last query block sees every key
+    if (CAUSAL) qblk = n_qblk - 1 - qblk;  // the last query block sees every key
   } else {
     const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     if (blk >= total) return;
@@ -100,7 +100,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
-  const size_t head = (size_t)bh * N * D;
+  // first row of this head; for packed sequences, of sequence b = bh / H in
+  // head h = bh % H (then N is that sequence's length and n_qblk covers the
+  // longest one)
+  size_t row0 = (size_t)bh * N;
+  if (seqs.cu) {
+    const int b = bh / seqs.H, hh = bh - b * seqs.H;
+    int s0, s1;
+    seq_range(seqs, b, s0, s1);
+    N = s1 - s0;
+    row0 = (size_t)hh * seqs.total + s0;
+    if (qblk * kBR >= N) return;  // past the end of a shorter sequence
+  }
+  const size_t head = row0 * D;
 
   const int q_start = qblk * kBR;
   const int q0w = q_start + 32 * wave;
@@ -138,8 +150,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
       qf[kk] = as_bf16x8(ld16(Qrow + 16 * kk + 8 * g));
       dof[kk] = as_bf16x8(ld16(Grow + 16 * kk + 8 * g));
     }
-    l2q = L2[(size_t)bh * N + qr];
-    dq_sc = Dsc[(size_t)bh * N + qr];
+    l2q = L2[row0 + qr];
+    dq_sc = Dsc[row0 + qr];
   }
 
   f32x16 dq_acc[NDB];
@@ -408,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch(const void* q, const void* k, const void* v, const void* dout, const float* l2, const float* dsc,
-                  float* dq, int BH, int N, float scale, const Dropout& drop, hipStream_t stream) {
+                  float* dq, int BH, int N, float scale, const Dropout& drop, const Seqs& sq, hipStream_t stream) {
   const int n_qblk = (N + kBR - 1) / kBR;
   const long long total = (long long)BH * n_qblk;
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
@@ -416,27 +428,31 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* dout,
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k), static_cast<const bf16_raw*>(v),
                      static_cast<const bf16_raw*>(dout), l2, dsc, dq, N, n_qblk, (int)total, scale, scale * kLog2e,
-                     drop);
+                     drop, sq);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_drop(const void* q, const void* k, const void* v, const void* dout, const float* l2,
-                       const float* dsc, float* dq, int BH, int N, float scale, const Dropout* drop,
+                       const float* dsc, float* dq, int BH, int N, float scale, const Dropout* drop, const Seqs& sq,
                        hipStream_t stream) {
-  if (drop) return launch<D, CAUSAL, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, *drop, stream);
-  return launch<D, CAUSAL, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, Dropout{}, stream);
+  if (drop) {
+    if (sq.cu) return hipErrorInvalidValue;  // dropout is offered for the dense layout only
+    return launch<D, CAUSAL, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, *drop, sq, stream);
+  }
+  return launch<D, CAUSAL, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, Dropout{}, sq, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
                               const float* dsc, float* dq, int BH, int N, int d, float scale, int causal,
-                              const Dropout* drop, hipStream_t stream) {
-  if (d == 128) return causal ? launch_drop<128, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, stream)
-                              : launch_drop<128, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, stream);
-  return causal ? launch_drop<64, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, stream)
-                : launch_drop<64, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, stream);
+                              const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+  const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
+  if (d == 128) return causal ? launch_drop<128, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, sq, stream)
+                              : launch_drop<128, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, sq, stream);
+  return causal ? launch_drop<64, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, sq, stream)
+                : launch_drop<64, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, sq, stream);
 }
 
 }  // namespace fa

@@ -136,6 +136,22 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int grid) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+// Packed variable-length sequences: Q, K, V (and O, L and the gradients) are
+// [H, total, d] head-major, and sequence b occupies rows cu[b] .. cu[b+1]-1
+// of every head.  cu == nullptr means the dense [B, H, N, d] layout.
+struct Seqs {
+  const int* cu;
+  int H;      // heads
+  int total;  // packed rows per head
+};
+// Rows [s0, s1) of sequence b, clamped into [0, total] and non-decreasing:
+// offsets out of order cost correctness, never an access outside the tensors.
+__device__ __forceinline__ void seq_range(const Seqs& sq, int b, int& s0, int& s1) {
+  const int a = min(max(sq.cu[b], 0), sq.total);
+  s0 = a;
+  s1 = min(max(sq.cu[b + 1], a), sq.total);
+}
+
 // Causal work items come in ranks of different length (the key range of a
 // query block, the query range of a key block), one item per head and rank.
 // Taking ids rank-major with the longest rank first -- id = rank * BH + head

@@ -192,7 +192,7 @@ template <int D, int DV, bool CAUSAL, int SPLIT, bool DROP>
 __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk, int n_qblk, int n_ksplit,
-    int tiles_per_split, int total, float c, Dropout dp) {
+    int tiles_per_split, int total, float c, Dropout dp, Seqs seqs) {
   constexpr int BC = FwdTile<D, DV>::BC;
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NKK = D / 16;    // 16-wide slices of the head dimension
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
 
   const int per_head = n_qblk * n_ksplit;
   int bh, rem;
-  if (CAUSAL) {
+  if (CAUSAL || seqs.cu) {
     if ((int)blockIdx.x >= total) return;
     longest_first(blockIdx.x, total / per_head, rem, bh);
   } else {
@@ -213,14 +213,26 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   int qb = rem / n_ksplit;
   const int ks = rem - qb * n_ksplit;
   if (CAUSAL) qb = n_qblk - 1 - qb;  // longest rows first
+  // first rows of this head in Q, in K / V and in O / L; for packed
+  // sequences, of sequence b = bh / H in head h = bh % H (then Nq = Nk is
+  // that sequence's length and n_qblk covers the longest one)
+  size_t q_row0 = (size_t)bh * Nq, k_row0 = (size_t)bh * Nk, o_row0 = ((size_t)ks * BH + bh) * Nq;
+  if (seqs.cu) {
+    const int b = bh / seqs.H, h = bh - b * seqs.H;
+    int s0, s1;
+    seq_range(seqs, b, s0, s1);
+    Nq = Nk = s1 - s0;
+    q_row0 = k_row0 = o_row0 = (size_t)h * seqs.total + s0;
+    if (qb * kBR >= Nq) return;  // past the end of a shorter sequence
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = (tid >> 6) & (kWaves - 1);  // query wave: rows 32 wave .. + 31
   const int half = SPLIT == 1 ? 0 : (tid >> 8);  // key range of this wave
   const int g = lane >> 5, col = lane & 31;
-  const bf16_raw* Qh = Q + (size_t)bh * Nq * D;
-  const bf16_raw* Kh = K + (size_t)bh * Nk * D;
-  const bf16_raw* Vh = V + (size_t)bh * Nk * DV;
+  const bf16_raw* Qh = Q + q_row0 * D;
+  const bf16_raw* Kh = K + k_row0 * D;
+  const bf16_raw* Vh = V + k_row0 * DV;
 
   const int q_start = qb * kBR;
   const int q0w = q_start + 32 * wave;
@@ -444,7 +456,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   const float l_nrm = halves_sum(l_rnd);
   if (my_q < Nq) {
     const float inv = l_nrm > 0.f ? (DROP ? dp.r : 1.f) / l_nrm : 0.f;
-    float* Orow = O + ((size_t)ks * BH + bh) * Nq * DV + (size_t)my_q * DV;
+    float* Orow = O + (o_row0 + my_q) * DV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -456,7 +468,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
         v.w = oacc[db][4 * i4 + 3] * inv;
         *reinterpret_cast<float4*>(Orow + 32 * db + 8 * i4 + 4 * g) = v;
       }
-    if (g == 0) LSE[((size_t)ks * BH + bh) * Nq + my_q] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (g == 0) LSE[o_row0 + my_q] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -496,7 +508,7 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restr
 
 template <int D, int DV, bool CAUSAL, bool DROP>
 hipError_t launch(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
-                  int n_ksplit, float* ws, float scale, const Dropout& dp, hipStream_t stream) {
+                  int n_ksplit, float* ws, float scale, const Dropout& dp, const Seqs& seqs, hipStream_t stream) {
   constexpr int BC = FwdTile<D, DV>::BC;
   const int n_qblk = (Nq + kBR - 1) / kBR;
   const int n_ktiles = (Nk + BC - 1) / BC;
@@ -516,12 +528,12 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
     hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 2, DROP>), dim3(grid), dim3(2 * kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
                        static_cast<const bf16_raw*>(v), o_dst, l_dst, BH, Nq, Nk, n_qblk, n_ksplit, tiles_per_split,
-                       (int)total, scale * kLog2e, dp);
+                       (int)total, scale * kLog2e, dp, seqs);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 1, DROP>), dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
                        static_cast<const bf16_raw*>(v), o_dst, l_dst, BH, Nq, Nk, n_qblk, n_ksplit, tiles_per_split,
-                       (int)total, scale * kLog2e, dp);
+                       (int)total, scale * kLog2e, dp, seqs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_ksplit == 1) return e;
   const long long rows = (long long)BH * Nq;
@@ -535,15 +547,17 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
 
 template <int D, bool CAUSAL>
 hipError_t launch_dv(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
-                     int dv, int n_ksplit, float* ws, float scale, const Dropout* drop, hipStream_t stream) {
-  // dropout is offered for the square contract (dv = d) only
+                     int dv, int n_ksplit, float* ws, float scale, const Dropout* drop, const Seqs& seqs,
+                     hipStream_t stream) {
+  // dropout is offered for the square dense contract (dv = d) only
   if (drop) {
-    if (dv != D) return hipErrorInvalidValue;
-    return launch<D, D, CAUSAL, true>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, *drop, stream);
+    if (dv != D || seqs.cu) return hipErrorInvalidValue;
+    return launch<D, D, CAUSAL, true>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, *drop, seqs, stream);
   }
   const Dropout none{};
-  return dv == 128 ? launch<D, 128, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, stream)
-                   : launch<D, 64, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, stream);
+  return dv == 128
+             ? launch<D, 128, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, seqs, stream)
+             : launch<D, 64, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, seqs, stream);
 }
 
 }  // namespace
@@ -566,12 +580,14 @@ int fwd_splitkv_resolve(int BH, int Nq, int Nk, int d, int dv, int n_splits) {
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq,
                            int Nk, int d, int dv, int causal, int n_ksplit, float* ws, float scale,
-                           const Dropout* drop, hipStream_t stream) {
+                           const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+  const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
+  if (sq.cu && n_ksplit != 1) return hipErrorInvalidValue;
   if (d == 128)
-    return causal ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, stream)
-                  : launch_dv<128, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, stream);
-  return causal ? launch_dv<64, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, stream)
-                : launch_dv<64, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, stream);
+    return causal ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, stream)
+                  : launch_dv<128, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, stream);
+  return causal ? launch_dv<64, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, stream)
+                : launch_dv<64, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, stream);
 }
 
 }  // namespace fa

@@ -10,6 +10,10 @@ namespace fa {
 // Dropout parameters (fa_dropout.h); a null pointer means no dropout.  The
 // kernels with dropout exist for the square contract (Nq = Nk, dv = d).
 struct Dropout;
+// Packed variable-length sequences (fa_common.h); a null pointer means the
+// dense [B, H, N, d] layout.  With sequences, BH is the number of (sequence,
+// head) units B * H and N the longest sequence: it sizes the grid.
+struct Seqs;
 
 // Forward, bf16 inputs: Q [BH, Nq, d], K [BH, Nk, d], V [BH, Nk, dv].
 // n_ksplit > 1 cuts the key tiles into that many ranges processed by separate
@@ -17,7 +21,7 @@ struct Dropout;
 // results (fwd_splitkv_resolve gives the count actually used).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq,
                            int Nk, int d, int dv, int causal, int n_ksplit, float* ws, float scale,
-                           const Dropout* drop, hipStream_t stream);
+                           const Dropout* drop, const Seqs* seqs, hipStream_t stream);
 // Number of key ranges a split-KV forward uses for n_splits requested
 // (0: chosen for the grid); 1 means no split and no workspace.
 int fwd_splitkv_resolve(int BH, int Nq, int Nk, int d, int dv, int n_splits);
@@ -29,7 +33,7 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 // L log2(e) and scale * D written by the backward preprocess.
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
                               const float* dsc, float* dq, int BH, int N, int d, float scale, int causal,
-                              const Dropout* drop, hipStream_t stream);
+                              const Dropout* drop, const Seqs* seqs, hipStream_t stream);
 
 // Backward phases (fa_bwd.hip); ws holds [scale * D | L log2(e)], BH * N
 // floats each.
@@ -37,10 +41,11 @@ hipError_t launch_bwd_prep(const void* dout, const float* o, const float* lse, f
                            float scale, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws,
                            float* dk, float* dv, int BH, int N, int d, float scale, int causal, const Dropout* drop,
-                           hipStream_t stream);
+                           const Seqs* seqs, hipStream_t stream);
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* dvec, int BH, int N,
-                           int d, float scale, int causal, const Dropout* drop, hipStream_t stream);
+                           int d, float scale, int causal, const Dropout* drop, const Seqs* seqs,
+                           hipStream_t stream);
 
 }  // namespace fa

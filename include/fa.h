@@ -167,6 +167,33 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, 
                    float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream);
 
 /*
+ * Packed variable-length sequences: instead of padding every sequence to the
+ * longest one, sequences share one token axis ("Padding is silent waste",
+ * FlashAttention: The Matrix You Never Have to Write Down, PyTorch API notes).
+ *   q, k, v    : device, bf16 [H, total, d] head-major; sequence b occupies
+ *                rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head
+ *   o          : device, float32 [H, total, d];  lse : float32 [H, total]
+ *   cu_seqlens : device, int32 [B+1], non-decreasing, cu[0] = 0, cu[B] = total
+ *   max_seqlen : host bound on the longest sequence (sizes the launch; rows of
+ *                a longer sequence beyond it are left unwritten); <= total
+ * Each row attends to the keys of its own sequence; causal masking is
+ * upper-left within the sequence; a sequence of length 0 has no rows.
+ * Offsets that break the rules give unspecified values for the rows
+ * involved, never a memory access outside the tensors (the kernels clamp
+ * them into [0, total]).  fa_bwd_varlen returns the gradients in the same
+ * layout; its workspace is fa_bwd_workspace_bytes(1, H, total, d).  Errors
+ * as fa_fwd / fa_bwd (negative sizes or max_seqlen > total: FA_ERR_SHAPE;
+ * NULL cu_seqlens: FA_ERR_NULL).
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
+                  const int* cu_seqlens, int B, int H, int total, int max_seqlen, int d,
+                  float scale, int causal, hipStream_t stream);
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                  const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                  const int* cu_seqlens, int B, int H, int total, int max_seqlen, int d,
+                  float scale, int causal, hipStream_t stream);
+
+/*
  * The three phases fa_bwd runs, for callers that schedule or time them
  * separately (same arguments, layouts and errors as fa_bwd; workspace as
  * sized by fa_bwd_workspace_bytes).  fa_bwd(...) is exactly
