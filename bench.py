@@ -14,6 +14,9 @@ Also reported on the same line:
              32768 keys, B=1, H=32, d=dv=128, against the HBM roofline
   dropout    the step's forward and backward with dropout p = 0.1
              (fa_fwd_dropout + fa_bwd_dropout, mask regenerated from the seed)
+  varlen     fwd+bwd over 8 packed causal sequences of mixed lengths (H=16,
+             d=128; fa_fwd_varlen + fa_bwd_varlen) against the same batch
+             padded to the longest sequence in the dense layout
   phases     forward and backward of the step timed separately
   kernels    each kernel of the step timed alone through its C entry point
              (fa_fwd, fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq)
@@ -235,6 +238,38 @@ def main():
     ms_drop = time_calls(step_drop, args.steps, stream)
     ms_drop_fwd = time_calls(fwd_drop, args.steps, stream)
 
+    # ------------------------------------------------------------ packed variable-length batch
+    lens = [4096, 3000, 2048, 1500, 1024, 700, 512, 300]
+    Hv, dv_ = 16, 128
+    total = sum(lens)
+    gv = torch.Generator("cpu").manual_seed(7)
+    qv, kv, vv, dov = (torch.randn((Hv, total, dv_), generator=gv).to(torch.bfloat16).to(dev) for _ in range(4))
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(lens)), dtype=torch.int32, device=dev)
+    ov = torch.empty((Hv, total, dv_), dtype=torch.float32, device=dev)
+    lv = torch.empty((Hv, total), dtype=torch.float32, device=dev)
+    wsv = torch.empty((fa.library().fa_bwd_workspace_bytes(1, Hv, total, dv_),), dtype=torch.uint8, device=dev)
+
+    def step_var():
+        fa.forward_varlen(qv, kv, vv, cu, max(lens), causal=True, out=ov, lse=lv)
+        fa.backward_varlen(qv, kv, vv, ov, lv, dov, cu, max(lens), causal=True, workspace=wsv)
+
+    Np = max(lens)  # the same batch padded to the longest sequence, dense layout
+    qp, kp, vp, dop = (torch.zeros((len(lens), Hv, Np, dv_), dtype=torch.bfloat16, device=dev) for _ in range(4))
+    op = torch.empty((len(lens), Hv, Np, dv_), dtype=torch.float32, device=dev)
+    lp = torch.empty((len(lens), Hv, Np), dtype=torch.float32, device=dev)
+    wsp = torch.empty((fa.library().fa_bwd_workspace_bytes(len(lens), Hv, Np, dv_),), dtype=torch.uint8, device=dev)
+
+    def step_pad():
+        fa.forward(qp, kp, vp, causal=True, out=op, lse=lp)
+        fa.backward(qp, kp, vp, op, lp, dop, causal=True, workspace=wsp)
+
+    for _ in range(3):
+        step_var()
+        step_pad()
+    ms_var = time_calls(step_var, args.steps, stream)
+    ms_pad = time_calls(step_pad, args.steps, stream)
+    var_flop = 3.5 * sum(4.0 * Hv * L * L * dv_ / 2 for L in lens)
+
     res = {
         "metric": "attention TFLOP/s (fwd, fwd+bwd) bf16 at 1 MI355X; % of MFMA peak",
         "value": round(value, 2),
@@ -311,6 +346,14 @@ def main():
             "fwd_ms": round(ms_drop_fwd, 4),
             "fwd_tflops": round(w.fwd_flop() / (ms_drop_fwd * 1e-3) / 1e12, 2),
             "flop_convention": "same FLOP as the step without dropout",
+        },
+        "varlen": {
+            "workload": "varlen_bf16_causal_h16d128_lens" + "-".join(map(str, lens)),
+            "step_ms": round(ms_var, 4),
+            "step_tflops": round(var_flop / (ms_var * 1e-3) / 1e12, 2),
+            "padded_dense_step_ms": round(ms_pad, 4),
+            "speedup_over_padding": round(ms_pad / ms_var, 3),
+            "flop_convention": "attention FLOP of the real (unpadded) sequences, 3.5x the causal forward",
         },
         "timed_wall_s": round(wall, 3),
     }
