@@ -310,8 +310,9 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
     if (t + 1 < t_end)
       issue_tiles<D, DV>(sm.k[half][(it + 1) & 1], sm.v[half][(it + 1) & 1], krs, vrs, key0 + BC, tc, wave);
     // a wave whose 32 rows all lie past the last query (few query rows, as in
-    // decoding, or the ragged last block) only helps copy the tiles
-    if (q0w >= Nq) continue;
+    // decoding, or the ragged last block), or (causal) before the tile's
+    // first key, only helps copy the tiles
+    if (q0w >= Nq || (CAUSAL && key0 > q0w + 31)) continue;
     tile_scores<D, BC>(s_cur, reinterpret_cast<const char*>(sm.k[half][it & 1]), kaddr, qf, ak);
 
     const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > Nk;
