@@ -72,6 +72,9 @@ def library():
         lib.fa_fwd_varlen.restype = i
         lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
         lib.fa_bwd_varlen.restype = i
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, f, i, vp]
+        lib.fa_fwd_strided.restype = i
         lib.fa_status_string.argtypes = [i]
         lib.fa_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -82,11 +85,13 @@ def status_string(status):
     return library().fa_status_string(int(status)).decode()
 
 
-def _check(q, k, v, square=True):
+def _check(q, k, v, square=True, strided=False):
     """Input contract: the page's single-head checks, extended to [B, H, N, d].
 
     square=False admits the page's general shapes, Q [B,H,Nq,d], K [B,H,Nk,d],
     V [B,H,Nk,dv]; square=True also requires Nq == Nk and dv == d.
+    strided=True admits views whose head-dim stride is 1 (the others may be
+    anything the strided forward accepts).
     """
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("Q, K, V must be rank 4 [B, H, N, d]")
@@ -111,10 +116,13 @@ def _check(q, k, v, square=True):
     if square and (q.shape != k.shape or k.shape != v.shape):
         raise ValueError(f"Q, K, V must share one [B, H, N, d] shape, got {tuple(q.shape)}, "
                          f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if strided:
+        if any(t.stride(-1) != 1 for t in (q, k, v)):
+            raise ValueError("Q, K, V must have unit stride along the head dimension")
+    elif not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("Q, K, V must be contiguous")
     if q.device.type != "cuda":
         raise ValueError("Q, K, V must be GPU tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("Q, K, V must be contiguous")
 
 
 def _ptr(t):
@@ -146,17 +154,23 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
 
     L is the natural-log logsumexp of the scaled, masked scores of each row.
     bf16 inputs run the matrix-core kernel (fa_fwd for one shared [B,H,N,d]
-    shape, fa_fwd_ex for Nq != Nk or dv != d); float32 inputs run the float32
-    kernel (fa_fwd_f32, one shared shape).  Causal masking is upper-left.
+    shape, fa_fwd_ex for Nq != Nk or dv != d, fa_fwd_strided for views such as
+    slices of a packed QKV tensor); float32 inputs run the float32 kernel
+    (fa_fwd_f32, one shared contiguous shape).  Causal masking is upper-left.
     ``out``/``lse`` may be preallocated.
     """
-    _check(q, k, v, square=q.dtype != torch.bfloat16)
+    bf16 = q.dtype == torch.bfloat16
+    _check(q, k, v, square=not bf16, strided=bf16)
     B, H, Nq, d = q.shape
     Nk, dv = k.shape[2], v.shape[3]
     o, l = _outputs(q, v, out, lse)
     lib = library()
     sc, cz, stream = _scale(scale, d), int(bool(causal)), _stream(q.device)
-    if q.dtype == torch.float32:
+    if bf16 and not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        arr = lambda t: (ctypes.c_int64 * 3)(*t.stride()[:3])
+        name, st = "fa_fwd_strided", lib.fa_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, Nq, Nk,
+                                                        d, dv, arr(q), arr(k), arr(v), sc, cz, stream)
+    elif q.dtype == torch.float32:
         name, st = "fa_fwd_f32", lib.fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, Nq, d, sc, cz,
                                                 stream)
     elif Nq == Nk and dv == d:

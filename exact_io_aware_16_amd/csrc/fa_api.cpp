@@ -60,6 +60,19 @@ int check_varlen(int B, int H, int total, int max_seqlen, int d, int causal, boo
   return FA_OK;
 }
 
+// Strided inputs: element strides (batch, head, row) >= 0, multiples of 8
+// (16-byte rows), a row stride no smaller than the row, tensors 16-byte
+// aligned, and one head's K / V rows byte-addressable in 31 bits.
+int check_strides(const void* p, const int64_t* st, int n_rows, int width) {
+  if (!st) return FA_ERR_NULL;
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0) return FA_ERR_SHAPE;
+  if (st[2] < width || st[2] > INT32_MAX) return FA_ERR_SHAPE;
+  if ((double)n_rows * (double)st[2] * 2.0 > (double)INT32_MAX) return FA_ERR_SHAPE;
+  if (p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
@@ -121,6 +134,24 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,
   if (!o || !lse || (Nk > 0 && (!q || !k || !v))) return FA_ERR_NULL;
   return hip_status(
       fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, scale, nullptr, nullptr, stream));
+}
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int Nq, int Nk,
+                   int d, int dv, const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                   float scale, int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape_ex(B, H, Nq, Nk, d, dv, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if ((st = check_strides(q, q_strides, Nq, d)) != FA_OK) return st;
+  if ((st = check_strides(k, k_strides, Nk, d)) != FA_OK) return st;
+  if ((st = check_strides(v, v_strides, Nk, dv)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!o || !lse || (Nk > 0 && (!q || !k || !v))) return FA_ERR_NULL;
+  const fa::Strides lay{q_strides[0], q_strides[1], k_strides[0], k_strides[1], v_strides[0], v_strides[1],
+                        (int)q_strides[2],  (int)k_strides[2],  (int)v_strides[2],  H};
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, scale, nullptr,
+                                        nullptr, stream, &lay));
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dv, int n_splits) {

@@ -104,19 +104,22 @@ struct TileCopy {
   static constexpr int KSLOTS = D / 8, VSLOTS = DV / 8;
   static constexpr int KINSTR = BC * KSLOTS / kThreads, VINSTR = BC * VSLOTS / kThreads;
   uint32_t k_off[KINSTR], v_off[VINSTR];
+  uint32_t k_row, v_row;  // bytes between consecutive K / V rows in global memory
 
-  __device__ __forceinline__ void init(int wave, int lane) {
+  __device__ __forceinline__ void init(int wave, int lane, int k_stride, int v_stride) {
+    k_row = (uint32_t)k_stride * 2u;
+    v_row = (uint32_t)v_stride * 2u;
 #pragma unroll
     for (int i = 0; i < KINSTR; ++i) {
       const int r = (i * kWaves + wave) * (64 / KSLOTS) + lane / KSLOTS;
       const int slot = lane % KSLOTS;
-      k_off[i] = (uint32_t)(((r & ~31) + perm32(r & 31)) * D * 2 + 16 * (slot ^ kswz<D>(r)));
+      k_off[i] = (uint32_t)((r & ~31) + perm32(r & 31)) * k_row + (uint32_t)(16 * (slot ^ kswz<D>(r)));
     }
 #pragma unroll
     for (int i = 0; i < VINSTR; ++i) {
       const int r = (i * kWaves + wave) * (64 / VSLOTS) + lane / VSLOTS;
       const int slot = lane % VSLOTS;
-      v_off[i] = (uint32_t)(r * DV * 2 + 16 * (slot ^ vswz<DV>(r)));
+      v_off[i] = (uint32_t)r * v_row + (uint32_t)(16 * (slot ^ vswz<DV>(r)));
     }
   }
 };
@@ -145,10 +148,10 @@ __device__ __forceinline__ void issue_tiles(bf16_raw* k_tile, bf16_raw* v_tile, 
   const uint32_t kbase = lds_addr_of(k_tile), vbase = lds_addr_of(v_tile);
 #pragma unroll
   for (int i = 0; i < TileCopy<D, DV>::KINSTR; ++i)
-    lds_copy16(krs, tc.k_off[i] + (uint32_t)key0 * D * 2, 0u, kbase + (uint32_t)(i * kWaves + wave) * 1024u);
+    lds_copy16(krs, tc.k_off[i] + (uint32_t)key0 * tc.k_row, 0u, kbase + (uint32_t)(i * kWaves + wave) * 1024u);
 #pragma unroll
   for (int i = 0; i < TileCopy<D, DV>::VINSTR; ++i)
-    lds_copy16(vrs, tc.v_off[i] + (uint32_t)key0 * DV * 2, 0u, vbase + (uint32_t)(i * kWaves + wave) * 1024u);
+    lds_copy16(vrs, tc.v_off[i] + (uint32_t)key0 * tc.v_row, 0u, vbase + (uint32_t)(i * kWaves + wave) * 1024u);
 }
 
 // S^T (BC keys x 32 queries) = K Q^T from one LDS K tile.  kaddr[kk] is the
@@ -192,7 +195,7 @@ template <int D, int DV, bool CAUSAL, int SPLIT, bool DROP>
 __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Nq, int Nk, int n_qblk, int n_ksplit,
-    int tiles_per_split, int total, float c, Dropout dp, Seqs seqs) {
+    int tiles_per_split, int total, float c, Dropout dp, Seqs seqs, Strides lay) {
   constexpr int BC = FwdTile<D, DV>::BC;
   constexpr int NKB = BC / 32;   // 32-key blocks per tile
   constexpr int NKK = D / 16;    // 16-wide slices of the head dimension
@@ -230,9 +233,25 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   const int wave = (tid >> 6) & (kWaves - 1);  // query wave: rows 32 wave .. + 31
   const int half = SPLIT == 1 ? 0 : (tid >> 8);  // key range of this wave
   const int g = lane >> 5, col = lane & 31;
-  const bf16_raw* Qh = Q + q_row0 * D;
-  const bf16_raw* Kh = K + k_row0 * D;
-  const bf16_raw* Vh = V + k_row0 * DV;
+  // this head's Q, K, V: packed sequences are dense rows of one head;
+  // otherwise batch / head / row strides (dense tensors pass dense strides)
+  const bf16_raw *Qh, *Kh, *Vh;
+  int q_stride, k_stride, v_stride;
+  if (seqs.cu) {
+    Qh = Q + q_row0 * D;
+    Kh = K + k_row0 * D;
+    Vh = V + k_row0 * DV;
+    q_stride = k_stride = D;
+    v_stride = DV;
+  } else {
+    const int b = bh / lay.H, h = bh - b * lay.H;
+    Qh = Q + (size_t)(b * lay.qb + h * lay.qh);
+    Kh = K + (size_t)(b * lay.kb + h * lay.kh);
+    Vh = V + (size_t)(b * lay.vb + h * lay.vh);
+    q_stride = lay.qr;
+    k_stride = lay.kr;
+    v_stride = lay.vr;
+  }
 
   const int q_start = qb * kBR;
   const int q0w = q_start + 32 * wave;
@@ -251,10 +270,12 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   const int t_end = min(ks_first + n_tiles, t_first + n_iter);
 
   TileCopy<D, DV> tc;
-  tc.init(wave, lane);
+  tc.init(wave, lane, k_stride, v_stride);
   // per-head buffer descriptors: reads past the head's last key return 0
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, Nk * D * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, Nk * DV * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, (int)((uint32_t)Nk * tc.k_row), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, (int)((uint32_t)Nk * tc.v_row), 0x00020000);
   // prologue loads: first K and V tile of the range
   if (t_first < t_end) issue_tiles<D, DV>(sm.k[half][0], sm.v[half][0], krs, vrs, t_first * BC, tc, wave);
 
@@ -275,7 +296,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   {
     const int qr = min(my_q, Nq - 1);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(ld16(Qh + (size_t)qr * D + 16 * kk + 8 * g));
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(ld16(Qh + (size_t)qr * q_stride + 16 * kk + 8 * g));
   }
 
   f32x16 oacc[NDB];
@@ -512,7 +533,8 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restr
 
 template <int D, int DV, bool CAUSAL, bool DROP>
 hipError_t launch(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
-                  int n_ksplit, float* ws, float scale, const Dropout& dp, const Seqs& seqs, hipStream_t stream) {
+                  int n_ksplit, float* ws, float scale, const Dropout& dp, const Seqs& seqs, const Strides& lay,
+                  hipStream_t stream) {
   constexpr int BC = FwdTile<D, DV>::BC;
   const int n_qblk = (Nq + kBR - 1) / kBR;
   const int n_ktiles = (Nk + BC - 1) / BC;
@@ -532,12 +554,12 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
     hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 2, DROP>), dim3(grid), dim3(2 * kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
                        static_cast<const bf16_raw*>(v), o_dst, l_dst, BH, Nq, Nk, n_qblk, n_ksplit, tiles_per_split,
-                       (int)total, scale * kLog2e, dp, seqs);
+                       (int)total, scale * kLog2e, dp, seqs, lay);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 1, DROP>), dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
                        static_cast<const bf16_raw*>(v), o_dst, l_dst, BH, Nq, Nk, n_qblk, n_ksplit, tiles_per_split,
-                       (int)total, scale * kLog2e, dp, seqs);
+                       (int)total, scale * kLog2e, dp, seqs, lay);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_ksplit == 1) return e;
   const long long rows = (long long)BH * Nq;
@@ -552,16 +574,17 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
 template <int D, bool CAUSAL>
 hipError_t launch_dv(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
                      int dv, int n_ksplit, float* ws, float scale, const Dropout* drop, const Seqs& seqs,
-                     hipStream_t stream) {
+                     const Strides& lay, hipStream_t stream) {
   // dropout is offered for the square dense contract (dv = d) only
   if (drop) {
     if (dv != D || seqs.cu) return hipErrorInvalidValue;
-    return launch<D, D, CAUSAL, true>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, *drop, seqs, stream);
+    return launch<D, D, CAUSAL, true>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, *drop, seqs, lay, stream);
   }
   const Dropout none{};
-  return dv == 128
-             ? launch<D, 128, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, seqs, stream)
-             : launch<D, 64, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, seqs, stream);
+  return dv == 128 ? launch<D, 128, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, seqs,
+                                                   lay, stream)
+                   : launch<D, 64, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, seqs, lay,
+                                                  stream);
 }
 
 }  // namespace
@@ -584,14 +607,18 @@ int fwd_splitkv_resolve(int BH, int Nq, int Nk, int d, int dv, int n_splits) {
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq,
                            int Nk, int d, int dv, int causal, int n_ksplit, float* ws, float scale,
-                           const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+                           const Dropout* drop, const Seqs* seqs, hipStream_t stream, const Strides* strides) {
   const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
-  if (sq.cu && n_ksplit != 1) return hipErrorInvalidValue;
+  if (sq.cu && (n_ksplit != 1 || strides)) return hipErrorInvalidValue;
+  // dense [BH, N, d] unless strides are given
+  const Strides lay = strides ? *strides
+                              : Strides{0, (long long)Nq * d, 0, (long long)Nk * d, 0, (long long)Nk * dv, d, d, dv, BH};
   if (d == 128)
-    return causal ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, stream)
-                  : launch_dv<128, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, stream);
-  return causal ? launch_dv<64, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, stream)
-                : launch_dv<64, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, stream);
+    return causal
+               ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, stream)
+               : launch_dv<128, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, stream);
+  return causal ? launch_dv<64, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, stream)
+                : launch_dv<64, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, stream);
 }
 
 }  // namespace fa

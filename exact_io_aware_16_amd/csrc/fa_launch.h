@@ -15,13 +15,23 @@ struct Dropout;
 // head) units B * H and N the longest sequence: it sizes the grid.
 struct Seqs;
 
+// Element strides of the forward's inputs: batch, head and row of Q, K and V
+// (the head-dim stride is 1).  A null pointer means dense [B, H, N, d]
+// tensors.  With strides, BH = B * H and H is needed to split it.
+struct Strides {
+  long long qb, qh, kb, kh, vb, vh;
+  int qr, kr, vr;
+  int H;
+};
+
 // Forward, bf16 inputs: Q [BH, Nq, d], K [BH, Nk, d], V [BH, Nk, dv].
 // n_ksplit > 1 cuts the key tiles into that many ranges processed by separate
 // workgroups; ws then holds n_ksplit * BH * Nq * (dv + 1) floats of partial
 // results (fwd_splitkv_resolve gives the count actually used).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq,
                            int Nk, int d, int dv, int causal, int n_ksplit, float* ws, float scale,
-                           const Dropout* drop, const Seqs* seqs, hipStream_t stream);
+                           const Dropout* drop, const Seqs* seqs, hipStream_t stream,
+                           const Strides* strides = nullptr);
 // Number of key ranges a split-KV forward uses for n_splits requested
 // (0: chosen for the grid); 1 means no split and no workspace.
 int fwd_splitkv_resolve(int BH, int Nq, int Nk, int d, int dv, int n_splits);

@@ -90,6 +90,23 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,
               int B, int H, int Nq, int Nk, int d, int dv, float scale, int causal, hipStream_t stream);
 
 /*
+ * The general forward on strided inputs: Q, K, V may be views (for example
+ * slices of one packed QKV projection), as the page's flash_attention takes
+ * any tensor ("Build it").  Same contract and outputs as fa_fwd_ex, plus
+ *   q_strides, k_strides, v_strides : host arrays of 3 element strides
+ *     (batch, head, row) of Q, K, V; the head-dim stride is 1.
+ * Each stride must be >= 0 and a multiple of 8 (16-byte rows), a row stride
+ * at least the row width (d, or dv for V) and below 2^31, one head's rows
+ * byte-addressable in 31 bits (N * row stride * 2 < 2^31), and q, k, v
+ * 16-byte aligned; otherwise FA_ERR_SHAPE (NULL stride arrays: FA_ERR_NULL).
+ * O and lse are dense [B,H,Nq,dv] and [B,H,Nq].
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, float* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, int dv,
+                   const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                   float scale, int causal, hipStream_t stream);
+
+/*
  * Split-KV forward (Flash-Decoding, "What it doesn't solve" on the first
  * page): for few query rows and long key sequences, the key tiles are cut
  * into contiguous ranges that separate workgroups process in parallel; each

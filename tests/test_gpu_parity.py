@@ -334,3 +334,52 @@ def test_fwdbwd_4k_d128_causal_full():
     check_fwd(o.cpu().numpy(), l.cpu().numpy(), oref, lref, w.name + " fwd")
     got = run_bwd(t, w.causal)
     check_bwd(got, oracle_bwd(t, w.causal, w.scale), w.name)
+
+
+# ------------------------------------------------------------------ strided inputs (fa_fwd_strided)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_strided_views_of_packed_qkv(d, causal):
+    """Q, K, V as views of one packed [B, N, 3, H, d] projection (row stride
+    3 H d, head stride d): same numbers as the contiguous copies, and the
+    oracle's."""
+    B, H, N = 2, 3, 300
+    g = torch.Generator("cpu").manual_seed(800 + d)
+    qkv = torch.randn((B, N, 3, H, d), generator=g).to(torch.bfloat16)
+    views = [qkv[:, :, j].permute(0, 2, 1, 3) for j in range(3)]  # [B, H, N, d] views
+    assert not views[0].is_contiguous()
+    say(f"strided packed QKV d={d} causal={causal}")
+    gqkv = qkv.cuda()
+    gviews = [gqkv[:, :, j].permute(0, 2, 1, 3) for j in range(3)]
+    o_s, l_s = fa.forward(*gviews, causal=causal)
+    o_c, l_c = fa.forward(*[x.contiguous() for x in gviews], causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_c) and torch.equal(l_s, l_c)
+    oref, lref = oracle.attention_forward_bhnd(*[x.contiguous().to(torch.float64).numpy() for x in views],
+                                               1 / math.sqrt(d), causal)
+    check_fwd(o_s.cpu().numpy(), l_s.cpu().numpy(), oref, lref, f"strided d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_strided_general_shapes(causal):
+    """Tq != Tk and dv != d with K, V sliced from wider buffers and Q taken
+    with a head stride larger than its rows (padded heads)."""
+    B, H, Nq, Nk, d, dv = 1, 2, 200, 333, 128, 64
+    g = torch.Generator("cpu").manual_seed(811)
+    qbuf = torch.randn((B, H, Nq + 8, d), generator=g).to(torch.bfloat16)
+    kbuf = torch.randn((B, Nk, H, d + 64), generator=g).to(torch.bfloat16)
+    vbuf = torch.randn((B, Nk, H, 2 * dv), generator=g).to(torch.bfloat16)
+    q = qbuf[:, :, 4:4 + Nq]                            # head stride (Nq + 8) d
+    k = kbuf[..., 64:].permute(0, 2, 1, 3)              # row stride H (d + 64), 128-byte offset
+    v = vbuf[..., :dv].permute(0, 2, 1, 3)              # row stride 2 H dv
+    say(f"strided general causal={causal}")
+    # slice on the device so the views keep their padded strides
+    gq = qbuf.cuda()[:, :, 4:4 + Nq]
+    gk = kbuf.cuda()[..., 64:].permute(0, 2, 1, 3)
+    gv = vbuf.cuda()[..., :dv].permute(0, 2, 1, 3)
+    assert gk.stride() == (Nk * H * (d + 64), d + 64, H * (d + 64), 1)
+    o_s, l_s = fa.forward(gq, gk, gv, causal=causal)
+    torch.cuda.synchronize()
+    oref, lref = oracle.attention_forward_bhnd(*[x.contiguous().to(torch.float64).numpy() for x in (q, k, v)],
+                                               1 / math.sqrt(d), causal)
+    check_fwd(o_s.cpu().numpy(), l_s.cpu().numpy(), oref, lref, f"strided general causal={causal}")
