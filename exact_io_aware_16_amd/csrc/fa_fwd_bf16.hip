@@ -420,6 +420,10 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
     // O^T += V^T P^T, V^T operand via transpose reads of the row-major tile;
     // operand sets rotate per (key block, half) group
     const char* vtile = reinterpret_cast<const char*>(sm.v[half][it & 1]);
+    // the other wave on this SIMD is usually in its softmax here: raised
+    // issue priority keeps the matrix core fed through this product
+    // (measured 2% on the forward workloads)
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -442,6 +446,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
         for (int db = 0; db < NDB; ++db) pin(av[(grp_i + 1) & 1][db]);
         if (grp_i > 0) pin(pb[(grp_i - 1) >> 1][(grp_i - 1) & 1]);
       }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   if constexpr (SPLIT == 2) {
