@@ -32,9 +32,16 @@ CFLAGS = [
 ]
 
 
+# Per-source flags.  The dQ kernel keeps every matrix-core result in VGPRs
+# (the vector ALUs read them there without copies) and only its Q / dO
+# operands in AGPRs; by default the compiler picks the AGPR form for every
+# product of a kernel that uses AGPRs at all.
+SOURCE_FLAGS = {"fa_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

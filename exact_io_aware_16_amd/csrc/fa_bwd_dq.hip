@@ -11,9 +11,14 @@
 //
 // Work split (one workgroup = 4 waves = 128 query rows of one head), the
 // mirror image of the forward kernel:
-//  * each wave owns 32 query rows; their Q and dO rows stay in registers as
-//    the B operands of S^T = K Q^T and dP^T = V dO^T (keys along M), so a
-//    query's values sit in one lane pair and its L and D are lane scalars;
+//  * each wave owns 32 query rows; their Q and dO rows stay in AGPRs as the
+//    B operands of S^T = K Q^T and dP^T = V dO^T (keys along M; the matrix
+//    core reads AGPR operands directly), so a query's values sit in one lane
+//    pair and its L and D are lane scalars;
+//  * every product result (S^T, dP^T, dQ^T) lives in VGPRs, where the vector
+//    ALUs read it without a copy: this file is built with the compiler's
+//    VGPR form for matrix-core results (-amdgpu-mfma-vgpr-form), and only
+//    the Q / dO operands are placed in AGPRs;
 //  * K and V tiles of BC keys arrive by LDS-direct buffer loads, triple
 //    buffered, rows in perm32 order with the backward's slot swizzle: the
 //    S^T / dP^T results then hold 8 consecutive keys per register octet --
@@ -150,6 +155,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
       qf[kk] = as_bf16x8(ld16(Qrow + 16 * kk + 8 * g));
       dof[kk] = as_bf16x8(ld16(Grow + 16 * kk + 8 * g));
     }
+    // in AGPRs for the whole kernel: they leave the VGPRs to the products
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      asm volatile("" : "+a"(qf[kk]));
+      asm volatile("" : "+a"(dof[kk]));
+    }
     l2q = L2[row0 + qr];
     dq_sc = Dsc[row0 + qr];
   }
@@ -235,14 +246,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   auto mfma_s = [&](int kb, int kk, const bf16x8(&o)[2]) {
     st[kb] = mfma32(o[0], qf[kk], kk == 0 ? f32x16{} : st[kb]);
     dpt[kb] = mfma32(o[1], dof[kk], kk == 0 ? f32x16{} : dpt[kb]);
-    anchor_a(st[kb]);
-    anchor_a(dpt[kb]);
+    anchor_v(st[kb]);
+    anchor_v(dpt[kb]);
   };
   auto mfma_q = [&](int kh, int pr, const bf16x8(&o)[2]) {
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       dq_acc[2 * pr + y] = mfma32(o[y], dsb[kh >> 1][kh & 1], dq_acc[2 * pr + y]);
-      anchor_a(dq_acc[2 * pr + y]);
+      anchor_v(dq_acc[2 * pr + y]);
     }
   };
   // group i of a dQ phase: half h = i / (NDB / 2), pair pr = i % (NDB / 2)
