@@ -48,20 +48,25 @@ def kernel_source_digest():
 
 
 def kernel_key(name):
-    """Short key for a (possibly mangled) kernel name, or None."""
-    m = re.search(r"fwd_bf16_kernel(?:ILi|<)(\d+)(?:ELi|, )(\d+)(?:ELb|, )(\d|true|false)(?:ELi|, )(\d)", name)
+    """Short key for a (possibly mangled) kernel name, or None.  The dropout
+    instantiations get their own keys ("_dropout")."""
+    b = r"(\d|true|false)"
+    m = re.search(r"fwd_bf16_kernel(?:ILi|<)(\d+)(?:ELi|, )(\d+)(?:ELb|, )" + b + r"(?:ELi|, )(\d)"
+                  r"(?:(?:ELb|, )" + b + r")?", name)
     if m:
         d, dv, causal, split = m.group(1), m.group(2), m.group(3) in ("1", "true"), m.group(4)
+        drop = m.group(5) in ("1", "true")
         return (f"fwd_d{d}" + (f"_dv{dv}" if dv != d else "") + ("_causal" if causal else "")
-                + ("_split2" if split == "2" else ""))
+                + ("_split2" if split == "2" else "") + ("_dropout" if drop else ""))
     m = re.search(r"splitkv_merge_kernel(?:ILi|<)(\d+)", name)
     if m:
         return f"splitkv_merge_dv{m.group(1)}"
     for kern, short in (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq")):
-        m = re.search(kern + r"(?:ILi|<)(\d+)(?:ELb|, )(\d|true|false)", name)
+        m = re.search(kern + r"(?:ILi|<)(\d+)(?:ELb|, )" + b + r"(?:(?:ELb|, )" + b + r")?", name)
         if m:
             causal = m.group(2) in ("1", "true")
-            return f"{short}_d{m.group(1)}" + ("_causal" if causal else "")
+            drop = m.group(3) in ("1", "true")
+            return f"{short}_d{m.group(1)}" + ("_causal" if causal else "") + ("_dropout" if drop else "")
     m = re.search(r"bwd_pre_kernel(?:ILi|<)(\d+)", name)
     if m:
         return f"bwd_pre_d{m.group(1)}"
@@ -248,10 +253,12 @@ def markdown_stats(stats, args):
            "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_stats -o run -- "
            "python -u $REPO/bench.py --no-cpu-baseline --steps 20 --warmup 5",
            "```", "",
-           "The bench runs the fwd+bwd step (B=2,H=16,N=4096,d=128 causal), then each of its kernels",
-           "alone on the same inputs, then the forward workload B=1,H=8,N=4096,d=128, then the decode",
-           "workload (B=1, H=32, one query row, 32768 keys, d=128: fwd_d128 with key ranges across",
-           "workgroups, then splitkv_merge_dv128).",
+           "The bench first runs the fwd+bwd step (B=2,H=16,N=4096,d=128 causal) untimed for about a",
+           "second, then each of its kernels alone on the same inputs, then the timed steps, then the",
+           "forward workload B=1,H=8,N=4096,d=128, the decode workload (B=1, H=32, one query row, 32768",
+           "keys, d=128: fwd_d128 with key ranges across workgroups, then splitkv_merge_dv128), and the",
+           "dropout (p = 0.1) and packed-sequence steps.  The step's kernels therefore average over",
+           "about 1500 calls; the dropout instantiations are listed under their own keys.",
            "Algorithmic TFLOP/s counts the attention products the method needs (forward 2, backward 5);",
            "executed TFLOP/s counts what the kernel runs (the dQ kernel recomputes S and dP).", "",
            "| kernel | calls | average us | min us | max us | algorithmic TFLOP/s | executed TFLOP/s |",
