@@ -139,19 +139,27 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// The tile offset is added to the per-lane offset, which the hardware range
-// checks against the head's size; the scalar offset stays 0.
+// One K and one V tile (BC keys from key0) of a head.  The descriptors start
+// at the tile's first row and span the rest of the head, so the lane offsets
+// stay loop invariant and the hardware range check still zeroes reads past
+// the head's last key; the scalar offset stays 0.
 template <int D, int DV>
-__device__ __forceinline__ void issue_tiles(bf16_raw* k_tile, bf16_raw* v_tile, __amdgpu_buffer_rsrc_t krs,
-                                            __amdgpu_buffer_rsrc_t vrs, int key0, const TileCopy<D, DV>& tc,
+__device__ __forceinline__ void issue_tiles(bf16_raw* k_tile, bf16_raw* v_tile, const bf16_raw* Kh,
+                                            const bf16_raw* Vh, int Nk, int key0, const TileCopy<D, DV>& tc,
                                             int wave) {
+  key0 = __builtin_amdgcn_readfirstlane(key0);  // wave-uniform: scalar arithmetic
+  const uint32_t kb0 = (uint32_t)key0 * tc.k_row, vb0 = (uint32_t)key0 * tc.v_row;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)Kh + kb0), (short)0, (int)((uint32_t)Nk * tc.k_row - kb0), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)Vh + vb0), (short)0, (int)((uint32_t)Nk * tc.v_row - vb0), 0x00020000);
   const uint32_t kbase = lds_addr_of(k_tile), vbase = lds_addr_of(v_tile);
 #pragma unroll
   for (int i = 0; i < TileCopy<D, DV>::KINSTR; ++i)
-    lds_copy16(krs, tc.k_off[i] + (uint32_t)key0 * tc.k_row, 0u, kbase + (uint32_t)(i * kWaves + wave) * 1024u);
+    lds_copy16(krs, tc.k_off[i], 0u, kbase + (uint32_t)(i * kWaves + wave) * 1024u);
 #pragma unroll
   for (int i = 0; i < TileCopy<D, DV>::VINSTR; ++i)
-    lds_copy16(vrs, tc.v_off[i] + (uint32_t)key0 * tc.v_row, 0u, vbase + (uint32_t)(i * kWaves + wave) * 1024u);
+    lds_copy16(vrs, tc.v_off[i], 0u, vbase + (uint32_t)(i * kWaves + wave) * 1024u);
 }
 
 // S^T (BC keys x 32 queries) = K Q^T from one LDS K tile.  kaddr[kk] is the
@@ -271,13 +279,8 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
 
   TileCopy<D, DV> tc;
   tc.init(wave, lane, k_stride, v_stride);
-  // per-head buffer descriptors: reads past the head's last key return 0
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, (int)((uint32_t)Nk * tc.k_row), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, (int)((uint32_t)Nk * tc.v_row), 0x00020000);
   // prologue loads: first K and V tile of the range
-  if (t_first < t_end) issue_tiles<D, DV>(sm.k[half][0], sm.v[half][0], krs, vrs, t_first * BC, tc, wave);
+  if (t_first < t_end) issue_tiles<D, DV>(sm.k[half][0], sm.v[half][0], Kh, Vh, Nk, t_first * BC, tc, wave);
 
   // loop-invariant lane parts of the LDS operand addresses (bytes)
   int kaddr[NKK];
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
     __syncthreads();
     if (t >= t_end) continue;  // the shorter key range idles through the barriers
     if (t + 1 < t_end)
-      issue_tiles<D, DV>(sm.k[half][(it + 1) & 1], sm.v[half][(it + 1) & 1], krs, vrs, key0 + BC, tc, wave);
+      issue_tiles<D, DV>(sm.k[half][(it + 1) & 1], sm.v[half][(it + 1) & 1], Kh, Vh, Nk, key0 + BC, tc, wave);
     // a wave whose 32 rows all lie past the last query (few query rows, as in
     // decoding, or the ragged last block), or (causal) before the tile's
     // first key, only helps copy the tiles
