@@ -279,8 +279,11 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
 
   TileCopy<D, DV> tc;
   tc.init(wave, lane, k_stride, v_stride);
+  // the wave index in a scalar register: the copies' LDS addresses (M0) are
+  // then scalar arithmetic
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   // prologue loads: first K and V tile of the range
-  if (t_first < t_end) issue_tiles<D, DV>(sm.k[half][0], sm.v[half][0], Kh, Vh, Nk, t_first * BC, tc, wave);
+  if (t_first < t_end) issue_tiles<D, DV>(sm.k[half][0], sm.v[half][0], Kh, Vh, Nk, t_first * BC, tc, wave_s);
 
   // loop-invariant lane parts of the LDS operand addresses (bytes)
   int kaddr[NKK];
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
     __syncthreads();
     if (t >= t_end) continue;  // the shorter key range idles through the barriers
     if (t + 1 < t_end)
-      issue_tiles<D, DV>(sm.k[half][(it + 1) & 1], sm.v[half][(it + 1) & 1], Kh, Vh, Nk, key0 + BC, tc, wave);
+      issue_tiles<D, DV>(sm.k[half][(it + 1) & 1], sm.v[half][(it + 1) & 1], Kh, Vh, Nk, key0 + BC, tc, wave_s);
     // a wave whose 32 rows all lie past the last query (few query rows, as in
     // decoding, or the ragged last block), or (causal) before the tile's
     // first key, only helps copy the tiles
