@@ -166,14 +166,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int my_key = k0 + 32 * wave + col;
 
   const int head_bytes = N * D * 2;
-  const __amdgpu_buffer_rsrc_t qrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head), (short)0, head_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t grs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head), (short)0, head_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t lrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(L2 + row0), (short)0, N * 4, 0x00020000);
-  const __amdgpu_buffer_rsrc_t drs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(Dsc + row0), (short)0, N * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(K + head), (short)0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -181,19 +173,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   QCopy<D> qc;
   qc.init(wave, lane);
-  // Q / dO / L2 / scale*D of one query tile into buffer b
-  // (the tile offset goes into the range-checked per-lane offset, so rows
-  // past the end of the head read as zeros)
+  // the wave index in a scalar register: the copies' LDS addresses (M0) are
+  // scalar arithmetic
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  // Q / dO / L2 / scale*D of one query tile into buffer b.  The descriptors
+  // start at the tile's first row and span the rest of the head, so the lane
+  // offsets stay loop invariant and rows past the end of the head read as
+  // zeros.
   auto issue_qtile = [&](uint32_t b, int q0) {
-    const uint32_t toff = (uint32_t)q0 * D * 2;
+    q0 = __builtin_amdgcn_readfirstlane(q0);
+    const uint32_t toff = (uint32_t)q0 * D * 2, rest = (uint32_t)head_bytes - toff;
+    const __amdgpu_buffer_rsrc_t qt =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head + (size_t)q0 * D), (short)0, (int)rest, 0x00020000);
+    const __amdgpu_buffer_rsrc_t gt =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head + (size_t)q0 * D), (short)0, (int)rest, 0x00020000);
     const uint32_t qb = lds_addr_of(sm.q[b]), gb = lds_addr_of(sm.dout[b]);
 #pragma unroll
     for (int i = 0; i < QCopy<D>::INSTR; ++i) {
-      lds_copy(qrs, qc.off[i] + toff, 0u, qb + (uint32_t)(i * kWaves + wave) * 1024u);
-      lds_copy(grs, qc.off[i] + toff, 0u, gb + (uint32_t)(i * kWaves + wave) * 1024u);
+      lds_copy(qt, qc.off[i], 0u, qb + (uint32_t)(i * kWaves + wave_s) * 1024u);
+      lds_copy(gt, qc.off[i], 0u, gb + (uint32_t)(i * kWaves + wave_s) * 1024u);
     }
-    if (wave == 0) lds_copy4(lrs, (uint32_t)(q0 + lane) * 4u, 0u, lds_addr_of(sm.l2[b]));
-    if (wave == 1) lds_copy4(drs, (uint32_t)(q0 + lane) * 4u, 0u, lds_addr_of(sm.dsc[b]));
+    if (wave_s < 2) {
+      const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((wave_s == 0 ? L2 : Dsc) + row0 + q0), (short)0, (N - q0) * 4, 0x00020000);
+      lds_copy4(rt, (uint32_t)lane * 4u, 0u, lds_addr_of(wave_s == 0 ? sm.l2[b] : sm.dsc[b]));
+    }
   };
 
   const int q_first = CAUSAL ? k0 : 0;  // k0 is a multiple of kBQ

@@ -126,19 +126,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int n_tiles = (kv_end + BC - 1) / BC;
 
   const int head_bytes = N * D * 2;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head), (short)0, head_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head), (short)0, head_bytes, 0x00020000);
   KvCopy<D> kc;
   kc.init(wave, lane);
+  // the wave index in a scalar register: the copies' LDS addresses (M0) are
+  // scalar arithmetic
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  // K and V of one key tile into buffer b.  The descriptors start at the
+  // tile's first row and span the rest of the head, so the lane offsets stay
+  // loop invariant and rows past the end of the head read as zeros.
   auto issue_tile = [&](uint32_t b, int key0) {
-    const uint32_t toff = (uint32_t)key0 * D * 2;
+    key0 = __builtin_amdgcn_readfirstlane(key0);
+    const uint32_t rest = (uint32_t)head_bytes - (uint32_t)key0 * D * 2;
+    const __amdgpu_buffer_rsrc_t kt =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + head + (size_t)key0 * D), (short)0, (int)rest, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vt =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + head + (size_t)key0 * D), (short)0, (int)rest, 0x00020000);
     const uint32_t kb = lds_addr_of(sm.k[b]), vb = lds_addr_of(sm.v[b]);
 #pragma unroll
     for (int i = 0; i < KvCopy<D>::INSTR; ++i) {
-      lds_copy(krs, kc.off[i] + toff, 0u, kb + (uint32_t)(i * kWaves + wave) * 1024u);
-      lds_copy(vrs, kc.off[i] + toff, 0u, vb + (uint32_t)(i * kWaves + wave) * 1024u);
+      lds_copy(kt, kc.off[i], 0u, kb + (uint32_t)(i * kWaves + wave_s) * 1024u);
+      lds_copy(vt, kc.off[i], 0u, vb + (uint32_t)(i * kWaves + wave_s) * 1024u);
     }
   };
   issue_tile(0u, 0);
