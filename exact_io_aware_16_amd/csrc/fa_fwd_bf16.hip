@@ -133,7 +133,16 @@ __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, uint32_t
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
                : "memory");
 }
-__device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(0) as the compiler's own wait instruction (vmcnt 0, expcnt 7,
+// lgkmcnt 15 in the gfx9 encoding), so its wait-count tracking knows that
+// every earlier vector memory load has completed and adds no wait of its
+// own for registers loaded before (an asm wait is opaque to it, and it then
+// kept a vmcnt(0) in every iteration, which also waited for the copies just
+// issued for the next tile); the empty asm keeps memory accesses in place.
+__device__ __forceinline__ void wait_tile_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
