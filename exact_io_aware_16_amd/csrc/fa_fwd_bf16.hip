@@ -174,24 +174,28 @@ __device__ __forceinline__ void issue_tiles(bf16_raw* k_tile, bf16_raw* v_tile, 
 // S^T (BC keys x 32 queries) = K Q^T from one LDS K tile.  kaddr[kk] is the
 // lane's byte offset of its 16-byte operand for head-dim slice kk in key
 // block 0; key block kb adds the constant 32 * kb rows.  K operands rotate
-// through the two sets of ak (see pin()); the set used last stays live for
-// the caller to release once the scores have been consumed.
+// through the two sets of ak (see pin()), loaded one group ahead; the set
+// used last stays live for the caller to release once the scores have been
+// consumed.
 template <int D, int BC>
 __device__ __forceinline__ void tile_scores(f32x16 (&s)[BC / 32], const char* ktile, const int (&kaddr)[D / 16],
                                             const bf16x8 (&qf)[D / 16], bf16x8 (&ak)[2][BC / 32]) {
   constexpr int NKB = BC / 32;
   constexpr int NKK = D / 16;
+  // the next group's operands load while this group's products run
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) ak[0][kb] = as_bf16x8(ld16(ktile + kaddr[0] + kb * 32 * D * 2));
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    bf16x8 (&a)[NKB] = ak[kk & 1];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) a[kb] = as_bf16x8(ld16(ktile + kaddr[kk] + kb * 32 * D * 2));
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(a[kb], qf[kk], kk == 0 ? f32x16{} : s[kb]);
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32(ak[kk & 1][kb], qf[kk], kk == 0 ? f32x16{} : s[kb]);
     // group kk is issued: the other set (group kk-1) may be overwritten from here on
     group_fence();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) pin(ak[(kk + 1) & 1][kb]);
+    if (kk + 1 < NKK)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) ak[(kk + 1) & 1][kb] = as_bf16x8(ld16(ktile + kaddr[kk + 1] + kb * 32 * D * 2));
   }
 }
 
@@ -439,27 +443,34 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
     // issue priority keeps the matrix core fed through this product
     // (measured 2% on the forward workloads)
     __builtin_amdgcn_s_setprio(2);
+    // V^T operands of group gi = (key block gi / 2, half gi % 2) into set gi % 2
+    auto load_v = [&](int gi) {
+      const int kb = gi >> 1, h = gi & 1;
+      bf16x8(&a)[NDB] = av[gi & 1];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        v4i16 part[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+          part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(vtile + vaddr[db] + (32 * kb + 16 * h + 4 * rr) * DV * 2));
+        a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    // the next group's operands load while this group's products run
+    load_v(0);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int grp_i = 2 * kb + h;
-        bf16x8 (&a)[NDB] = av[grp_i & 1];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          v4i16 part[2];
-#pragma unroll
-          for (int rr = 0; rr < 2; ++rr)
-            part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16*)(vtile + vaddr[db] + (32 * kb + 16 * h + 4 * rr) * DV * 2));
-          a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(a[db], pb[kb][h], oacc[db]);
+        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(av[grp_i & 1][db], pb[kb][h], oacc[db]);
         group_fence();
 #pragma unroll
         for (int db = 0; db < NDB; ++db) pin(av[(grp_i + 1) & 1][db]);
         if (grp_i > 0) pin(pb[(grp_i - 1) >> 1][(grp_i - 1) & 1]);
+        if (grp_i + 1 < 2 * NKB) load_v(grp_i + 1);
       }
     __builtin_amdgcn_s_setprio(0);
   }
