@@ -18,8 +18,9 @@ import os
 
 import torch
 
-__all__ = ["forward", "forward_splitkv", "backward", "backward_prep", "backward_dkdv", "backward_dq", "library", "FAError",
-           "LIB_PATH", "status_string"]
+__all__ = ["forward", "forward_splitkv", "backward", "backward_prep", "backward_dkdv", "backward_dq",
+           "forward_dropout", "backward_dropout", "forward_varlen", "backward_varlen", "workspace_for",
+           "library", "FAError", "LIB_PATH", "status_string"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
