@@ -161,6 +161,69 @@ def test_fwd_splitkv(nq, nk, splits, d, dv, causal):
     assert float((o - o1).abs().max()) <= 5e-3 and float((l - l1).abs().max()) <= 5e-4
 
 
+def _planted_max_range(nq, nk=None, device="cuda"):
+    """The longest key range one d = 128 head may have (Nk * d * 2 bytes just
+    below 2^31: 8388607 keys, a ragged last tile), with a closed-form answer.
+
+    Every key is the bulk key (-64 e_127, value all ones) except three planted
+    keys at the first, a middle and the last position (4 e_dir with dir 0, 1,
+    2, random bf16 values).  Every query holds 8 e_127, so a bulk key scores
+    -512 scale (weight about e^-45, negligible next to the planted keys even
+    summed over 8M keys), and each query puts an amplitude on some planted
+    directions.  The softmax of the first page is then a sum over four
+    classes of keys, evaluated in float64 on the host.  A read past the end
+    of K (a zero row, score 0) or of a wrong row would show at once.
+    """
+    d = 128
+    nk = nk or (2**31 - 1) // (d * 2)
+    pos = [0, nk // 2 + 5, nk - 1]
+    scale = 1.0 / math.sqrt(d)
+    rng = np.random.default_rng(2024)
+    vp = torch.tensor(rng.standard_normal((3, d)), dtype=torch.float32).to(torch.bfloat16)
+    # per row kind: amplitudes on directions 0, 1, 2
+    kinds = [(45, 0, 0), (0, 45, 0), (0, 0, 45), (40, 0, 40), (0, 0, 0), (0, -45, 30)]
+    qh = torch.zeros(1, 1, nq, d, dtype=torch.bfloat16)
+    for i in range(nq):
+        qh[0, 0, i, :3] = torch.tensor(kinds[i % len(kinds)], dtype=torch.bfloat16)
+        qh[0, 0, i, 127] = 8
+    k = torch.zeros(1, 1, nk, d, dtype=torch.bfloat16, device=device)
+    k[0, 0, :, 127] = -64
+    v = torch.ones(1, 1, nk, d, dtype=torch.bfloat16, device=device)
+    for j, p in enumerate(pos):
+        k[0, 0, p, 127] = 0
+        k[0, 0, p, j] = 4
+        v[0, 0, p] = vp[j].to(device)
+    # closed form in float64
+    qd = qh[0, 0].double().numpy()
+    s_p = scale * 4.0 * qd[:, :3]                      # [nq, 3] planted scores
+    s_b = scale * (qd[:, 127] * -64.0)                 # [nq] bulk score
+    n_b = nk - 3
+    m = np.maximum(s_p.max(axis=1), s_b)
+    w_p = np.exp(s_p - m[:, None])
+    w_b = n_b * np.exp(s_b - m)
+    den = w_p.sum(axis=1) + w_b
+    o_ref = (w_p @ vp.double().numpy() + w_b[:, None]) / den[:, None]
+    l_ref = m + np.log(den)
+    return qh, k, v, o_ref, l_ref
+
+
+def test_fwd_max_key_range_closed_form():
+    nq = 130  # two query blocks, the second ragged
+    say("fwd max key range: Nq130 Nk8388607 d128, dense and split-KV")
+    qh, k, v, o_ref, l_ref = _planted_max_range(nq)
+    o, l = fa.forward(qh.cuda(), k, v)
+    torch.cuda.synchronize()
+    eo, el = errs(o[0, 0].cpu(), o_ref), errs(l[0, 0].cpu(), l_ref)
+    say(f"dense: O max-abs {eo[0]:.3e} rel-L2 {eo[1]:.3e}  L max-abs {el[0]:.3e}")
+    assert eo[0] <= O_MAX and eo[1] <= O_REL and el[0] <= L_MAX, (eo, el)
+    # one query row per kind through the split-KV launch (decode form)
+    o, l = fa.forward_splitkv(qh[:, :, :6].contiguous().cuda(), k, v)
+    torch.cuda.synchronize()
+    eo, el = errs(o[0, 0].cpu(), o_ref[:6]), errs(l[0, 0].cpu(), l_ref[:6])
+    say(f"split-KV: O max-abs {eo[0]:.3e} rel-L2 {eo[1]:.3e}  L max-abs {el[0]:.3e}")
+    assert eo[0] <= O_MAX and eo[1] <= O_REL and el[0] <= L_MAX, (eo, el)
+
+
 def test_fwd_splitkv_decode_long_context():
     # decoding: one query row per head against 32768 keys, 32 heads
     t = I.make_general(1, 32, 1, 32768, 128, 128, 1100)
@@ -321,6 +384,33 @@ def test_bwd_phases_compose_to_fa_bwd(d, causal):
     torch.cuda.synchronize()
     for a_, b_ in ((dq, dq2), (dk, dk2), (dv, dv2)):
         assert torch.equal(a_, b_)
+
+
+def test_fwdbwd_heads_past_4gib():
+    # 70000 heads of 256 rows: every bf16 tensor spans 4.6 GB and every float32
+    # output 9.2 GB, so head bases sit past 2^32 bytes in all four kernels.
+    # The heads repeat 5 seeded source heads: the sampled heads must match the
+    # oracle of their source head and every head must equal its source bitwise.
+    n_src, B, H, N, d = 5, 2, 35000, 256, 128
+    w = I.Workload("heads_past_4gib_src", 61, 1, n_src, N, d, True, "bf16", backward=True)
+    t = I.make_inputs(w)
+    say(f"fwd+bwd B{B} H{H} N{N} d{d} causal: {n_src} source heads repeated")
+    idx = (torch.arange(B * H) % n_src).cuda()
+    q, k, v, do = (t[n].cuda()[0].index_select(0, idx).view(B, H, N, d) for n in ("q", "k", "v", "do"))
+    o, l = fa.forward(q, k, v, causal=True)
+    dq, dk, dv = fa.backward(q, k, v, o, l, do, causal=True)
+    torch.cuda.synchronize()
+    del q, k, v, do
+    oref, lref = oracle_fwd(t, True, w.scale)
+    gref = oracle_bwd(t, True, w.scale)
+    flat = [x.view(B * H, *x.shape[2:]) for x in (o, l, dq, dk, dv)]
+    for bh in (0, 1, B * H // 2 + 3, B * H - 2, B * H - 1):
+        s = bh % n_src
+        check_fwd(flat[0][bh].cpu().numpy(), flat[1][bh].cpu().numpy(), oref[0, s], lref[0, s], f"head {bh} fwd")
+        check_bwd([x[bh].cpu().numpy() for x in flat[2:]], [g[0, s] for g in gref], f"head {bh}")
+    for x in flat:
+        rep = x.view(B * H // n_src, n_src, *x.shape[1:])
+        assert torch.equal(rep, rep[:1].expand_as(rep))
 
 
 def test_fwdbwd_4k_d128_causal_full():
