@@ -75,6 +75,20 @@ def time_calls(fn, iters, stream):
     return start.elapsed_time(end) / iters
 
 
+def steady(fn, seconds):
+    """Untimed calls of fn() for about `seconds`, one at a time.  After host
+    work (input generation) the GPU has idled and its clock has dropped; a
+    few warmup calls are too short to bring it back, this is long enough."""
+    import torch
+
+    t0 = time.perf_counter()
+    for _ in range(100000):
+        fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 > seconds:
+            break
+
+
 def cpu_baseline(w, t, budget_s=12.0):
     """The oracle (untuned) on whole heads of the workload until ~budget_s of work."""
     import numpy as np
@@ -149,12 +163,7 @@ def main():
 
     # untimed: about a second of steps brings the GPU to its steady clock, so
     # that neither the parts nor the step below are timed during the ramp
-    t_warm = time.perf_counter()
-    for _ in range(2000):
-        step()
-        torch.cuda.synchronize()
-        if time.perf_counter() - t_warm > 1.0:
-            break
+    steady(step, 1.0)
 
     # each kernel of the step alone (workspace prepared once for the two passes)
     dq_o, dk_o, dv_o = (torch.empty_like(o) for _ in range(3))
@@ -208,6 +217,7 @@ def main():
     def fwd2():
         fa.forward(qf, kf, vf, causal=False, out=of, lse=lf)
 
+    steady(fwd2, 0.5)
     for _ in range(args.warmup):
         fwd2()
     ms_f2 = time_calls(fwd2, args.steps, stream)
@@ -226,6 +236,7 @@ def main():
     def dec():
         fa.forward_splitkv(qd, kd, vd, workspace=wsd, out=od, lse=ld)
 
+    steady(dec, 0.5)
     for _ in range(args.warmup):
         dec()
     ms_dec = time_calls(dec, args.steps, stream)
@@ -242,8 +253,7 @@ def main():
     def fwd_drop():
         fa.forward_dropout(q, k, v, 0.1, 2024, 0, causal=True, out=o, lse=lse)
 
-    for _ in range(3):
-        step_drop()
+    steady(step_drop, 0.5)
     ms_drop = time_calls(step_drop, args.steps, stream)
     ms_drop_fwd = time_calls(fwd_drop, args.steps, stream)
 
@@ -272,10 +282,9 @@ def main():
         fa.forward(qp, kp, vp, causal=True, out=op, lse=lp)
         fa.backward(qp, kp, vp, op, lp, dop, causal=True, workspace=wsp)
 
-    for _ in range(3):
-        step_var()
-        step_pad()
+    steady(step_var, 0.5)
     ms_var = time_calls(step_var, args.steps, stream)
+    steady(step_pad, 0.5)
     ms_pad = time_calls(step_pad, args.steps, stream)
     var_flop = 3.5 * sum(4.0 * Hv * L * L * dv_ / 2 for L in lens)
 
