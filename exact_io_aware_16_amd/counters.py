@@ -129,15 +129,28 @@ def _per_kernel_mean(rows, counter):
 
 
 def _read_stats(d):
-    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    out = {}
+    """Per-dispatch durations from the kernel trace, grouped by kernel key and
+    workgroup count: one kernel serves several workloads of the bench (the
+    step, the padded comparison batch, packed sequences), and only the launches
+    of one grid describe one workload."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    acc = {}
     for f in files:
         for r in csv.DictReader(open(f)):
-            key = kernel_key(r.get("Name", ""))
-            if key:
-                out[key] = {"calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
-                            "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
-    return out
+            key = kernel_key(r.get("Kernel_Name", ""))
+            if not key:
+                continue
+            wg = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            ns = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            a = acc.setdefault(f"{key}@{wg}", {"key": key, "workgroups": wg, "calls": 0, "sum_ns": 0.0,
+                                                "min_ns": ns, "max_ns": ns})
+            a["calls"] += 1
+            a["sum_ns"] += ns
+            a["min_ns"] = min(a["min_ns"], ns)
+            a["max_ns"] = max(a["max_ns"], ns)
+    for a in acc.values():
+        a["avg_ns"] = a.pop("sum_ns") / a["calls"]
+    return acc
 
 
 def summarize(args):
@@ -182,6 +195,10 @@ def summarize(args):
 
 
 _F5 = 2.0 * 32 * 4096 ** 2 * 128  # forward FLOP of B=2 H=16 N=4096 d=128 causal (two products)
+# workgroups of the launch each ALGORITHMIC entry describes: 128 query (or
+# key) rows per workgroup, 16 rows per workgroup for the prep kernel
+GRID = {"fwd_d128_split2": 8 * 32, "fwd_d128_causal": 32 * 32, "bwd_pre_d128": 32 * 4096 // 16,
+        "bwd_dkdv_d128_causal": 32 * 32, "bwd_dq_d128_causal": 32 * 32}
 ALGORITHMIC = {
     # key: (workload, algorithmic HBM bytes per launch, algorithmic FLOP per launch,
     #       FLOP the kernel executes per launch)
@@ -257,18 +274,28 @@ def markdown_stats(stats, args):
            "second, then each of its kernels alone on the same inputs, then the timed steps, then the",
            "forward workload B=1,H=8,N=4096,d=128, the decode workload (B=1, H=32, one query row, 32768",
            "keys, d=128: fwd_d128 with key ranges across workgroups, then splitkv_merge_dv128), and the",
-           "dropout (p = 0.1) and packed-sequence steps.  The step's kernels therefore average over",
-           "about 1500 calls; the dropout instantiations are listed under their own keys.",
-           "Algorithmic TFLOP/s counts the attention products the method needs (forward 2, backward 5);",
-           "executed TFLOP/s counts what the kernel runs (the dQ kernel recomputes S and dP).", "",
-           "| kernel | calls | average us | min us | max us | algorithmic TFLOP/s | executed TFLOP/s |",
-           "|---|---|---|---|---|---|---|"]
-    for k, v in sorted(stats.items()):
-        _, _, flop, xflop = ALGORITHMIC.get(k, ("", 0, 0, 0))
+           "dropout (p = 0.1) and packed-sequence steps, the latter beside the same batch padded to",
+           "B=8.  Each workload runs about half a second untimed before it is timed.  One kernel serves",
+           "several of these workloads, so launches are grouped by kernel and workgroup count, taken",
+           "from the per-dispatch trace.  Algorithmic TFLOP/s counts the attention products the method",
+           "needs (forward 2, backward 5); executed TFLOP/s counts what the kernel runs (the dQ kernel",
+           "recomputes S and dP).  Both are given for the launch of the workload named beside them.",
+           "Rows without a workload: 4096 workgroups are the packed batch and its padded copy (8",
+           "sequences x 16 heads x 32 blocks each), fwd_d128 at 512 and splitkv_merge_dv128 the decode",
+           "call, the _dropout keys the step with dropout, the other prep grids those of the packed and",
+           "padded batches.", "",
+           "| kernel | workgroups | workload | calls | average us | min us | max us | algorithmic TFLOP/s | "
+           "executed TFLOP/s |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for _, v in sorted(stats.items(), key=lambda kv: (kv[1]["key"], kv[1]["workgroups"])):
+        k = v["key"]
+        wl, _, flop, xflop = ALGORITHMIC.get(k, ("", 0, 0, 0))
+        if GRID.get(k) != v["workgroups"]:
+            wl, flop, xflop = "", 0, 0
         tf = f"{flop / (v['avg_ns'] * 1e-9) / 1e12:.1f}" if flop else ""
         xtf = f"{xflop / (v['avg_ns'] * 1e-9) / 1e12:.1f}" if xflop else ""
-        out.append(f"| {k} | {v['calls']} | {v['avg_ns'] / 1e3:.1f} | {v['min_ns'] / 1e3:.1f} | "
-                   f"{v['max_ns'] / 1e3:.1f} | {tf} | {xtf} |")
+        out.append(f"| {k} | {v['workgroups']} | {wl} | {v['calls']} | {v['avg_ns'] / 1e3:.1f} | "
+                   f"{v['min_ns'] / 1e3:.1f} | {v['max_ns'] / 1e3:.1f} | {tf} | {xtf} |")
     out.append("")
     return "\n".join(out)
 
