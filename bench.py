@@ -347,7 +347,7 @@ def main():
             "workload": dc["name"],
             "ms": round(ms_dec, 4),
             "roofline": {
-                "kernel": "fwd_bf16_kernel, key ranges across workgroups, + splitkv_merge_kernel (the fa_fwd_splitkv call)",
+                "kernel": "decode_kernel (key ranges across workgroups, vector ALUs) + splitkv_merge_kernel (the fa_fwd_splitkv call)",
                 "bound": "hbm",
                 "achieved": round(dec_gbs, 1),
                 "peak": HBM_PEAK_GBS,

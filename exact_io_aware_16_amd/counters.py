@@ -58,6 +58,9 @@ def kernel_key(name):
         drop = m.group(5) in ("1", "true")
         return (f"fwd_d{d}" + (f"_dv{dv}" if dv != d else "") + ("_causal" if causal else "")
                 + ("_split2" if split == "2" else "") + ("_dropout" if drop else ""))
+    m = re.search(r"decode_kernel(?:ILi|<)(\d+)(?:ELi|, )(\d)(?:ELb|, )" + b, name)
+    if m:
+        return f"decode_d{m.group(1)}_rows{m.group(2)}" + ("_causal" if m.group(3) in ("1", "true") else "")
     m = re.search(r"splitkv_merge_kernel(?:ILi|<)(\d+)", name)
     if m:
         return f"splitkv_merge_dv{m.group(1)}"

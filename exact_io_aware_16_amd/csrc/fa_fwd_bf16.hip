@@ -531,41 +531,62 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
 // Merges n_split partial (O_s, L_s) of each query row (written by the
 // forward with key ranges across workgroups) with the logsumexp identity:
 // L = m + ln sum_s e^(L_s - m), O = sum_s e^(L_s - L) O_s; rows whose
-// ranges all saw no key get O = 0, L = -inf.  One thread per 4 columns.
+// ranges all saw no key get O = 0, L = -inf.  One wave per row: lane s holds
+// the weight of ranges s, s + 64, ...; the columns' sums over the ranges run
+// with independent loads, so the merge costs a few memory round trips.
 template <int DV>
-__global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ Opart,
-                                                            const float* __restrict__ Lpart, float* __restrict__ O,
-                                                            float* __restrict__ LSE, long long rows, int n_split) {
-  constexpr int TPR = DV / 4;
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = gid / TPR;
-  const int part = (int)(gid % TPR);
-  if (row >= rows) return;
-  float m = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, Lpart[(size_t)sp * rows + row]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  if (m != -INFINITY) {
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float w = __expf(Lpart[(size_t)sp * rows + row] - m);
-      const float4 o = *reinterpret_cast<const float4*>(Opart + ((size_t)sp * rows + row) * DV + 4 * part);
-      acc.x += w * o.x;
-      acc.y += w * o.y;
-      acc.z += w * o.z;
-      acc.w += w * o.w;
-      den += w;
+__global__ __launch_bounds__(64) void splitkv_merge_kernel(const float* __restrict__ Opart,
+                                                           const float* __restrict__ Lpart, float* __restrict__ O,
+                                                           float* __restrict__ LSE, long long rows, int n_split) {
+  constexpr int CPL = DV / 64;  // columns per lane
+  const long long row = blockIdx.x;
+  const int lane = threadIdx.x;
+  float ls[4];  // n_split <= 256
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int sp = lane + 64 * r;
+    ls[r] = sp < n_split ? Lpart[(size_t)sp * rows + row] : -INFINITY;
+  }
+  float m = fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3]));
+#pragma unroll
+  for (int x = 32; x > 0; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
+  float ws[4], den = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    ws[r] = m == -INFINITY ? 0.f : __expf(ls[r] - m);
+    den += ws[r];
+  }
+#pragma unroll
+  for (int x = 32; x > 0; x >>= 1) den += __shfl_xor(den, x);
+  float acc[CPL];
+#pragma unroll
+  for (int cc = 0; cc < CPL; ++cc) acc[cc] = 0.f;
+  constexpr int U = 8;
+  for (int s0 = 0; s0 < n_split; s0 += U) {
+    float part[U][CPL], w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = min(s0 + u, n_split - 1);
+      w[u] = __shfl(ws[sp >> 6], sp & 63);
+      if (s0 + u >= n_split) w[u] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) part[u][cc] = Opart[((size_t)sp * rows + row) * DV + lane + 64 * cc];
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int cc = 0; cc < CPL; ++cc) acc[cc] = fmaf(w[u], part[u][cc], acc[cc]);
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  *reinterpret_cast<float4*>(O + (size_t)row * DV + 4 * part) =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (part == 0) LSE[row] = den > 0.f ? m + __logf(den) : -INFINITY;
+#pragma unroll
+  for (int cc = 0; cc < CPL; ++cc) O[(size_t)row * DV + lane + 64 * cc] = acc[cc] * inv;
+  if (lane == 0) LSE[row] = den > 0.f ? m + __logf(den) : -INFINITY;
 }
 
 template <int D, int DV, bool CAUSAL, bool DROP>
 hipError_t launch(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
                   int n_ksplit, float* ws, float scale, const Dropout& dp, const Seqs& seqs, const Strides& lay,
-                  hipStream_t stream) {
+                  bool dense, hipStream_t stream) {
   constexpr int BC = FwdTile<D, DV>::BC;
   const int n_qblk = (Nq + kBR - 1) / kBR;
   const int n_ktiles = (Nk + BC - 1) / BC;
@@ -581,7 +602,13 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
   // small for that (fewer than two workgroups per CU) splits each
   // workgroup's key tiles over 8 waves instead.
   const bool split = total < 2 * kComputeUnits && (n_ktiles + n_ksplit - 1) / n_ksplit > 1;
-  if (split)
+  // a few query rows against key ranges (decoding): the same ranges on the
+  // vector ALUs, which stream K and V at close to HBM speed
+  if (!DROP && dense && n_ksplit > 1 && !seqs.cu && decode_applies(Nq, D, DV)) {
+    const hipError_t ed = launch_decode_bf16(q, k, v, o_dst, l_dst, BH, Nq, Nk, D, n_ksplit, tiles_per_split * BC,
+                                             scale * kLog2e, CAUSAL ? 1 : 0, stream);
+    if (ed != hipSuccess) return ed;
+  } else if (split)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, DV, CAUSAL, 2, DROP>), dim3(grid), dim3(2 * kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
                        static_cast<const bf16_raw*>(v), o_dst, l_dst, BH, Nq, Nk, n_qblk, n_ksplit, tiles_per_split,
@@ -594,10 +621,8 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_ksplit == 1) return e;
   const long long rows = (long long)BH * Nq;
-  const long long threads = rows * (DV / 4);
-  const long long mgrid = (threads + 255) / 256;
-  if (mgrid > (1LL << 31) - 1) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((splitkv_merge_kernel<DV>), dim3((unsigned)mgrid), dim3(256), 0, stream, o_dst, l_dst, o, lse,
+  if (rows > (1LL << 31) - 1 || n_ksplit > 256) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((splitkv_merge_kernel<DV>), dim3((unsigned)rows), dim3(64), 0, stream, o_dst, l_dst, o, lse,
                      rows, n_ksplit);
   return hipGetLastError();
 }
@@ -605,17 +630,18 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
 template <int D, bool CAUSAL>
 hipError_t launch_dv(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
                      int dv, int n_ksplit, float* ws, float scale, const Dropout* drop, const Seqs& seqs,
-                     const Strides& lay, hipStream_t stream) {
+                     const Strides& lay, bool dense, hipStream_t stream) {
   // dropout is offered for the square dense contract (dv = d) only
   if (drop) {
     if (dv != D || seqs.cu) return hipErrorInvalidValue;
-    return launch<D, D, CAUSAL, true>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, *drop, seqs, lay, stream);
+    return launch<D, D, CAUSAL, true>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, *drop, seqs, lay, dense,
+                                      stream);
   }
   const Dropout none{};
   return dv == 128 ? launch<D, 128, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, seqs,
-                                                   lay, stream)
+                                                   lay, dense, stream)
                    : launch<D, 64, CAUSAL, false>(q, k, v, o, lse, BH, Nq, Nk, n_ksplit, ws, scale, none, seqs, lay,
-                                                  stream);
+                                                  dense, stream);
 }
 
 }  // namespace
@@ -644,12 +670,16 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o
   // dense [BH, N, d] unless strides are given
   const Strides lay = strides ? *strides
                               : Strides{0, (long long)Nq * d, 0, (long long)Nk * d, 0, (long long)Nk * dv, d, d, dv, BH};
+  const bool dense = strides == nullptr;
   if (d == 128)
-    return causal
-               ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, stream)
-               : launch_dv<128, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, stream);
-  return causal ? launch_dv<64, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, stream)
-                : launch_dv<64, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, stream);
+    return causal ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, dense,
+                                         stream)
+                  : launch_dv<128, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, dense,
+                                          stream);
+  return causal ? launch_dv<64, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, dense,
+                                      stream)
+                : launch_dv<64, false>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, dense,
+                                       stream);
 }
 
 }  // namespace fa

@@ -36,6 +36,17 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o
 // (0: chosen for the grid); 1 means no split and no workspace.
 int fwd_splitkv_resolve(int BH, int Nq, int Nk, int d, int dv, int n_splits);
 
+// Split-KV forward for 1 .. kDecodeMaxRows query rows with d == dv on the
+// vector ALUs (fa_decode.hip): one workgroup per (head, key range) of
+// keys_per_split keys writes its partial O rows to opart ([n_split][BH * Nq]
+// rows of d floats) and its logsumexp to lpart, the layout the split-KV merge
+// reads.  c = scale * log2(e).  Dense [BH, N, d] inputs only.
+constexpr int kDecodeMaxRows = 4;
+bool decode_applies(int Nq, int d, int dv);
+hipError_t launch_decode_bf16(const void* q, const void* k, const void* v, float* opart, float* lpart, int BH, int Nq,
+                              int Nk, int d, int n_split, int keys_per_split, float c, int causal,
+                              hipStream_t stream);
+
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N,
                           int d, float scale, int causal, hipStream_t stream);
 

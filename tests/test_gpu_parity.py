@@ -145,9 +145,12 @@ def test_fwd_no_keys_gives_zero_and_minus_inf(causal):
 
 
 # ------------------------------------------------------------------ split-KV across workgroups (fa_fwd_splitkv)
-@pytest.mark.parametrize("d,dv", [(128, 128), (64, 128), (128, 64)])
+# one to four query rows with d = dv take the vector-ALU key-range kernel,
+# the others the matrix-core kernel; both end in the same merge
+@pytest.mark.parametrize("d,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("nq,nk,splits", [(1, 4097, 0), (1, 4097, 3), (4, 8192, 16), (200, 3000, 5), (1, 64, 4)])
+@pytest.mark.parametrize("nq,nk,splits", [(1, 4097, 0), (1, 4097, 3), (4, 8192, 16), (3, 1000, 0), (200, 3000, 5),
+                                          (1, 64, 4)])
 def test_fwd_splitkv(nq, nk, splits, d, dv, causal):
     t = I.make_general(2, 2, nq, nk, d, dv, 1000 + nq + nk + splits + d)
     say(f"fwd splitkv Nq={nq} Nk={nk} splits={splits} d={d} dv={dv} causal={causal}")
@@ -216,12 +219,14 @@ def test_fwd_max_key_range_closed_form():
     eo, el = errs(o[0, 0].cpu(), o_ref), errs(l[0, 0].cpu(), l_ref)
     say(f"dense: O max-abs {eo[0]:.3e} rel-L2 {eo[1]:.3e}  L max-abs {el[0]:.3e}")
     assert eo[0] <= O_MAX and eo[1] <= O_REL and el[0] <= L_MAX, (eo, el)
-    # one query row per kind through the split-KV launch (decode form)
-    o, l = fa.forward_splitkv(qh[:, :, :6].contiguous().cuda(), k, v)
-    torch.cuda.synchronize()
-    eo, el = errs(o[0, 0].cpu(), o_ref[:6]), errs(l[0, 0].cpu(), l_ref[:6])
-    say(f"split-KV: O max-abs {eo[0]:.3e} rel-L2 {eo[1]:.3e}  L max-abs {el[0]:.3e}")
-    assert eo[0] <= O_MAX and eo[1] <= O_REL and el[0] <= L_MAX, (eo, el)
+    # one query row per kind through the split-KV launch (decode form), four
+    # rows and two rows per call
+    for r0, r1 in ((0, 4), (4, 6)):
+        o, l = fa.forward_splitkv(qh[:, :, r0:r1].contiguous().cuda(), k, v)
+        torch.cuda.synchronize()
+        eo, el = errs(o[0, 0].cpu(), o_ref[r0:r1]), errs(l[0, 0].cpu(), l_ref[r0:r1])
+        say(f"split-KV rows {r0}..{r1 - 1}: O max-abs {eo[0]:.3e} rel-L2 {eo[1]:.3e}  L max-abs {el[0]:.3e}")
+        assert eo[0] <= O_MAX and eo[1] <= O_REL and el[0] <= L_MAX, (eo, el)
 
 
 def test_fwd_splitkv_decode_long_context():
