@@ -276,7 +276,7 @@ def markdown_stats(stats, args):
            "The bench first runs the fwd+bwd step (B=2,H=16,N=4096,d=128 causal) untimed for about a",
            "second, then each of its kernels alone on the same inputs, then the timed steps, then the",
            "forward workload B=1,H=8,N=4096,d=128, the decode workload (B=1, H=32, one query row, 32768",
-           "keys, d=128: fwd_d128 with key ranges across workgroups, then splitkv_merge_dv128), and the",
+           "keys, d=128: decode_d128_rows1 on key ranges across workgroups, then splitkv_merge_dv128), and the",
            "dropout (p = 0.1) and packed-sequence steps, the latter beside the same batch padded to",
            "B=8.  Each workload runs about half a second untimed before it is timed.  One kernel serves",
            "several of these workloads, so launches are grouped by kernel and workgroup count, taken",
@@ -284,7 +284,7 @@ def markdown_stats(stats, args):
            "needs (forward 2, backward 5); executed TFLOP/s counts what the kernel runs (the dQ kernel",
            "recomputes S and dP).  Both are given for the launch of the workload named beside them.",
            "Rows without a workload: 4096 workgroups are the packed batch and its padded copy (8",
-           "sequences x 16 heads x 32 blocks each), fwd_d128 at 512 and splitkv_merge_dv128 the decode",
+           "sequences x 16 heads x 32 blocks each), decode_d128_rows1 and splitkv_merge_dv128 the decode",
            "call, the _dropout keys the step with dropout, the other prep grids those of the packed and",
            "padded batches.", "",
            "| kernel | workgroups | workload | calls | average us | min us | max us | algorithmic TFLOP/s | "

@@ -19,7 +19,7 @@
 //  * each lane group keeps its own running max m, sum l and output slice O
 //    over the keys it sees (the blocked recurrence of "From softmax to
 //    attention: rescale the output too"), rescaling once per chunk of CH keys;
-//  * the groups of a wave, then the four waves, are merged with the same
+//  * the groups of a wave, then the waves, are merged with the same
 //    identity, and the range's O / l and L = m + ln l are written once.
 // Causal masking is upper-left (query i sees keys 0 .. i), so with at most
 // four query rows only the first keys are ever visible; ranges past them
@@ -30,9 +30,9 @@
 namespace fa {
 namespace {
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecCh = 16;  // keys per lane group in flight
+constexpr int kDecCh = 8;   // keys per lane group in flight
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const bf16_raw* __r
     }
   }
   __syncthreads();
-  // then the four waves, and write this range's partial result
+  // then the waves, and write this range's partial result
   if (wave == 0 && lane < LPK) {
     const long long rows = (long long)BH * Nq;
 #pragma unroll
