@@ -14,8 +14,10 @@
 // arithmetic on the vector ALUs:
 //  * a key row of D bf16 is D / 8 lanes x 16 bytes; a wave covers 64 / (D / 8)
 //    keys per load, and each lane keeps CH keys of K and V in flight;
-//  * a lane group (the D / 8 lanes of one key) forms the dot product of its
-//    slices and sums it across the group with lane exchanges;
+//  * a lane group (the D / 8 lanes of one key) forms its slices of the dot
+//    products of CH keys and sums them across the group by a reduce-scatter,
+//    so that each lane ends with one key's score; one exponential per lane,
+//    and the weights go back to every lane of the group for the V update;
 //  * each lane group keeps its own running max m, sum l and output slice O
 //    over the keys it sees (the blocked recurrence of "From softmax to
 //    attention: rescale the output too"), rescaling once per chunk of CH keys;
@@ -52,6 +54,25 @@ __device__ __forceinline__ void unpack8(uint4 r, float (&f)[8]) {
   }
 }
 
+// Reduce-scatter of H values over the lane bits M, M / 2, ... (log2 H steps):
+// at each step the lane keeps the upper half of its values if its bit M is
+// set, else the lower half, and adds the partner's copy of the kept half.
+// Afterwards v[0] holds value sum over the exchanged lanes of the index
+// formed by the lane's bits M, M / 2, ... (most significant first).
+template <int M, int H>
+__device__ __forceinline__ void reduce_scatter(float (&v)[kDecCh], int sl) {
+  if constexpr (H > 1) {
+    const bool up = (sl & M) != 0;
+#pragma unroll
+    for (int t = 0; t < H / 2; ++t) {
+      const float send = up ? v[t] : v[t + H / 2];
+      const float keep = up ? v[t + H / 2] : v[t];
+      v[t] = keep + __shfl_xor(send, M);
+    }
+    reduce_scatter<M / 2, H / 2>(v, sl);
+  }
+}
+
 // (m, l, o) <- merge of two partial softmax states over disjoint key sets,
 // each with sums taken against its own reference max; m = -inf marks a state
 // that has seen no visible key (then l = 0, o = 0).
@@ -76,6 +97,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const bf16_raw* __r
                                                             int n_split, int keys_per_split, float c) {
   constexpr int LPK = D / 8;     // lanes per key row
   constexpr int KPW = 64 / LPK;  // keys per wave and load
+  constexpr int DUP = LPK / kDecCh;  // lanes holding each key after the reduce-scatter
+  static_assert(DUP >= 1, "a lane group must hold at least as many lanes as keys in flight");
   __shared__ float red_m[kDecWaves][NQ], red_l[kDecWaves][NQ];
   __shared__ float red_o[kDecWaves][NQ][D];
 
@@ -127,8 +150,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const bf16_raw* __r
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       if (i >= Nq) break;
-      // scores of this chunk's keys, in log2 units
-      float s[kDecCh];
+      // this lane's slice of the dot products of the chunk's keys
+      float v[kDecCh];
 #pragma unroll
       for (int j = 0; j < kDecCh; ++j) {
         float kf[8];
@@ -136,33 +159,47 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const bf16_raw* __r
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot = fmaf(qv[i][e], kf[e], dot);
-#pragma unroll
-        for (int x = LPK / 2; x > 0; x >>= 1) dot += __shfl_xor(dot, x);
-        const int key = base + j * KPW + grp;
-        const bool vis = key < k_end && (!CAUSAL || key <= i);
-        s[j] = vis ? dot * c : -INFINITY;
+        v[j] = dot;
       }
-      float mx = s[0];
+      // reduce-scatter across the group: at the exchange over lane bit M the
+      // lane keeps the half of its keys selected by that bit and adds the
+      // partner's slices of them; after log2(CH) exchanges lane sl holds key
+      // sl / DUP summed over the lanes that differ in the bits exchanged, and
+      // the remaining low bits are summed in full
+      reduce_scatter<LPK / 2, kDecCh>(v, sl);
 #pragma unroll
-      for (int j = 1; j < kDecCh; ++j) mx = fmaxf(mx, s[j]);
+      for (int x = DUP / 2; x > 0; x >>= 1) v[0] += __shfl_xor(v[0], x);
+      const int my_key = base + (sl / DUP) * KPW + grp;
+      const bool vis = my_key < k_end && (!CAUSAL || my_key <= i);
+      const float s_own = vis ? v[0] * c : -INFINITY;  // log2 units
+      float mx = s_own;
+#pragma unroll
+      for (int x = LPK / 2; x > 0; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
       const float m_new = fmaxf(m[i], mx);
       if (m_new == -INFINITY) continue;  // nothing visible to this group yet
       const float alpha = fast_exp2(m[i] - m_new);  // 0 while nothing was accumulated
       l[i] *= alpha;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[i][e] *= alpha;
+      const float p_own = fast_exp2(s_own - m_new);
+      if (sl % DUP == 0) l[i] += p_own;  // one lane per key adds its weight
 #pragma unroll
       for (int j = 0; j < kDecCh; ++j) {
-        const float p = fast_exp2(s[j] - m_new);
+        const float p = __shfl(p_own, grp * LPK + j * DUP);
         float vf[8];
         unpack8(vr[j], vf);
-        l[i] += p;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[i][e] = fmaf(p, vf[e], o[i][e]);
       }
       m[i] = m_new;
     }
   }
+
+  // each lane's l covers its own keys: sum over the group
+#pragma unroll
+  for (int i = 0; i < NQ; ++i)
+#pragma unroll
+    for (int x = LPK / 2; x > 0; x >>= 1) l[i] += __shfl_xor(l[i], x);
 
   // merge the KPW lane groups of the wave (lane bits above the slice index)
 #pragma unroll
