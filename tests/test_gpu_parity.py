@@ -150,8 +150,12 @@ def test_fwd_no_keys_gives_zero_and_minus_inf(causal):
 @pytest.mark.parametrize("d,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("nq,nk,splits", [(1, 4097, 0), (1, 4097, 3), (4, 8192, 16), (3, 1000, 0), (200, 3000, 5),
-                                          (1, 64, 4)])
+                                          (1, 64, 4), (2, 16400, 100), (1, 16384, 256), (40, 16400, 256)])
 def test_fwd_splitkv(nq, nk, splits, d, dv, causal):
+    # Up to 256 ranges: the merge keeps the weights of ranges s, s + 64,
+    # s + 128 and s + 192 in lane s.  Ranges are whole tiles (64 keys, or 128
+    # when d = dv = 64): 16384 keys with 256 requested give 256 ranges of one
+    # tile, 16400 keys give 129 of two, and 100 requested give 86 of three.
     t = I.make_general(2, 2, nq, nk, d, dv, 1000 + nq + nk + splits + d)
     say(f"fwd splitkv Nq={nq} Nk={nk} splits={splits} d={d} dv={dv} causal={causal}")
     q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
