@@ -112,7 +112,10 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, float* o, float*
  * into contiguous ranges that separate workgroups process in parallel; each
  * writes a partial (O, L) into `workspace`, and a second kernel merges them
  * with the logsumexp identity ("The identity").  Same contract and results
- * (up to rounding) as fa_fwd_ex.
+ * (up to rounding) as fa_fwd_ex.  With one to four query rows and d == dv the
+ * ranges run on the vector ALUs and weight V with unrounded float32
+ * probabilities; otherwise the matrix-core kernel rounds them to bf16 first,
+ * as fa_fwd_ex does.
  *   n_splits : 1 .. 256 ranges requested (capped at the number of key
  *              tiles), or 0 to let the library choose for the grid.
  *   workspace: device, >= fa_fwd_splitkv_workspace_bytes(...) bytes for the
