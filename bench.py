@@ -244,6 +244,10 @@ def main():
     dec_bytes = (bh * dc["Nq"] * dc["d"] * 2 + bh * dc["Nk"] * (dc["d"] + dc["dv"]) * 2
                  + bh * dc["Nq"] * (dc["dv"] + 1) * 4)
     dec_gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
+    # measured HBM bytes of the call: the key-range kernel and the merge
+    t_dec, dec_src = committed_traffic("decode_d128_rows1")
+    t_mrg, _ = committed_traffic("splitkv_merge_dv128")
+    dec_traffic = t_dec + t_mrg if t_dec is not None and t_mrg is not None else None
 
     # ------------------------------------------------------------ the step with dropout
     def step_drop():
@@ -353,7 +357,8 @@ def main():
                 "peak": HBM_PEAK_GBS,
                 "unit": "GB/s",
                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None,
+                "traffic": dec_traffic,
+                "traffic_source": dec_src,
                 "algorithmic_bytes_per_call": dec_bytes,
             },
         },

@@ -101,6 +101,14 @@ def run():
                 fa.backward(q, k, v, o, lse, do, causal=w.causal)
         torch.cuda.synchronize()
         print(f"ran {w.name}", flush=True)
+    # the decode workload: one query row per head against 32768 keys
+    dc = I.DECODE_32K
+    td = I.make_general(dc["B"], dc["H"], dc["Nq"], dc["Nk"], dc["d"], dc["dv"], dc["seed"])
+    qd, kd, vd = (td[n].to(dev) for n in ("q", "k", "v"))
+    for _ in range(REPEAT):
+        fa.forward_splitkv(qd, kd, vd)
+    torch.cuda.synchronize()
+    print(f"ran {dc['name']}", flush=True)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(REPEAT):
@@ -201,7 +209,8 @@ _F5 = 2.0 * 32 * 4096 ** 2 * 128  # forward FLOP of B=2 H=16 N=4096 d=128 causal
 # workgroups of the launch each ALGORITHMIC entry describes: 128 query (or
 # key) rows per workgroup, 16 rows per workgroup for the prep kernel
 GRID = {"fwd_d128_split2": 8 * 32, "fwd_d128_causal": 32 * 32, "bwd_pre_d128": 32 * 4096 // 16,
-        "bwd_dkdv_d128_causal": 32 * 32, "bwd_dq_d128_causal": 32 * 32}
+        "bwd_dkdv_d128_causal": 32 * 32, "bwd_dq_d128_causal": 32 * 32,
+        "decode_d128_rows1": 32 * 16, "splitkv_merge_dv128": 32}
 ALGORITHMIC = {
     # key: (workload, algorithmic HBM bytes per launch, algorithmic FLOP per launch,
     #       FLOP the kernel executes per launch)
@@ -220,6 +229,11 @@ ALGORITHMIC = {
     # S and dP are computed a second time (1.5x the forward executed)
     "bwd_dq_d128_causal": ("B=2 H=16 N=4096 d=128 causal",
                            4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 32 * 4096 * 128 * 4, 0.5 * _F5, 1.5 * _F5),
+    # decode, 16 key ranges: reads Q, K, V once, writes 16 partial (O, L) per row
+    "decode_d128_rows1": ("decode B=1 H=32 Nq=1 Nk=32768 d=128",
+                          32 * 128 * 2 + 2 * 32 * 32768 * 128 * 2 + 16 * 32 * 129 * 4, 0.0, 0.0),
+    # reads the 16 partials per row, writes O and L
+    "splitkv_merge_dv128": ("decode B=1 H=32 Nq=1 Nk=32768 d=128", 16 * 32 * 129 * 4 + 32 * 129 * 4, 0.0, 0.0),
 }
 
 
@@ -228,7 +242,8 @@ def markdown_counters(rec, args):
     out = ["# Hardware counters of the attention kernels (MI355X)", "",
            "Collected with the committed driver `exact_io_aware_16_amd/counters.py` (5 launches of each",
            "kernel on the forward workload B=1,H=8,N=4096,d=128 and the forward+backward workload",
-           "B=2,H=16,N=4096,d=128 causal, plus a 512 MiB device copy for calibration), one counter group",
+           "B=2,H=16,N=4096,d=128 causal, the decode call B=1,H=32, one query row, 32768 keys, d=128,",
+           "plus a 512 MiB device copy for calibration), one counter group",
            "per run:", "", "```",
            "cd /tmp && export TMPDIR=/tmp PYTHONPATH=$REPO",
            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o run -- python -u -m exact_io_aware_16_amd.counters run",
