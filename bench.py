@@ -129,7 +129,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this attention path has no multi-GPU mode "
-              "(heads and batch shard with no exchange; see the design notes). Run with --gpus 1.",
+              "(heads and batch shard across GPUs with no exchange between them). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
