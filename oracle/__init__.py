@@ -24,14 +24,16 @@ Functions and what pins each one (tests/test_oracle.py):
                       Pinned by central finite differences, by torch
                       autograd of a float64 softmax, and by the row-sum
                       invariants of dK and dV.
-  tiled_forward       the pages' blocked recurrence, used to show that the
-                      online rescale reaches the one-shot result.  Pinned by
-                      the two-block example, the late max, the causal tile
-                      counts (36/64, 528/1024) and equality with
-                      attention_forward on ragged block sizes.
-  streaming_logsumexp the one-pass (max, sum) reduction with its two guards.
-                      Pinned by the four-number example and the seeded
-                      1000-value example printed on the first page.
+  tiled_forward       the pages' blocked form: per-tile partial states merged
+                      by the logsumexp identity, used to show that the online
+                      rescale reaches the one-shot result.  Pinned by the
+                      two-block example, the late max, the causal tile counts
+                      (36/64, 528/1024) and equality with attention_forward
+                      on ragged block sizes.
+  logsumexp_by_blocks the one-pass (max, sum) reduction with its guards;
+  online_normalizer_trace  its per-block trace.  Pinned by the four-number
+                      example and the seeded 1000-value example printed on
+                      the first page.
   dropout (module)    dropout whose mask the backward regenerates from the
                       generator state ("Backward can recreate tiles", second
                       page): Philox4x32-10 pinned by its published
@@ -51,7 +53,7 @@ from .attention import (
     attention_forward_bhnd,
     attention_backward_bhnd,
     tiled_forward,
-    streaming_logsumexp,
+    logsumexp_by_blocks,
     online_normalizer_trace,
 )
 from . import dropout, varlen
@@ -62,7 +64,7 @@ __all__ = [
     "attention_forward_bhnd",
     "attention_backward_bhnd",
     "tiled_forward",
-    "streaming_logsumexp",
+    "logsumexp_by_blocks",
     "online_normalizer_trace",
     "dropout",
     "varlen",

@@ -163,97 +163,114 @@ def attention_backward_bhnd(q, k, v, do, scale, causal=False):
                  for t in range(4))
 
 
-def online_normalizer_trace(blocks):
-    """Running (max, sum, rescale factor) after each block of a score row.
+def _merge(state_a, state_b):
+    """Combine two partial softmax states over disjoint key sets.
 
-    The online normalizer of "The identity: you can fix what you already
-    wrote" (first page) and "Tiles need a shared softmax normalization"
-    (second page): when a block raises the maximum from m to m_new, the sum
-    kept so far is multiplied by e^(m - m_new) before the block's own terms
-    are added.  The factor is forced to 0 while the running max is still
-    -inf (nothing accumulated yet), and a block that is entirely -inf is
-    skipped.  Returns a list of (m, l, factor) tuples, one per block that
-    contributed.
+    A state (m, l, o) summarises a set of scores x_j (with values v_j) of one
+    row: m = max x_j, l = sum_j e^(x_j - m), o = sum_j e^(x_j - m) v_j.  The
+    identity of "The identity: you can fix what you already wrote" (first
+    page), used across tiles in "Tiles need a shared softmax normalization"
+    (second page): with m = max(m_a, m_b), the union has
+    l = e^(m_a - m) l_a + e^(m_b - m) l_b and likewise for o.  A set with no
+    finite score has m = -inf, l = 0, o = 0 and weight 0; works elementwise
+    on arrays of rows (o may be None when only (m, l) is tracked).
     """
-    m, l = _NEG_INF, 0.0
+    ma, la, oa = state_a
+    mb, lb, ob = state_b
+    m = np.maximum(ma, mb)
+    with np.errstate(invalid="ignore"):
+        wa = np.where(np.isneginf(ma), 0.0, np.exp(ma - np.where(np.isneginf(m), 0.0, m)))
+        wb = np.where(np.isneginf(mb), 0.0, np.exp(mb - np.where(np.isneginf(m), 0.0, m)))
+    l = wa * la + wb * lb
+    o = None if oa is None else np.asarray(wa)[..., None] * oa + np.asarray(wb)[..., None] * ob
+    return m, l, o
+
+
+def _block_state(x, vals=None):
+    """Partial state (m, l, o) of each row of a score block x (rows x keys)."""
+    x = np.asarray(x, dtype=np.float64)
+    m = x.max(axis=-1) if x.shape[-1] else np.full(x.shape[:-1], _NEG_INF)
+    shift = np.where(np.isneginf(m), 0.0, m)
+    e = np.exp(x - shift[..., None])  # -inf scores give exactly 0
+    l = e.sum(axis=-1)
+    return m, l, (None if vals is None else e @ vals)
+
+
+def online_normalizer_trace(blocks):
+    """Running (max, sum, factor) of one score row consumed block by block.
+
+    After each block that holds a finite score, the running state is merged
+    with the block's own state; ``factor`` is the multiplier the merge applies
+    to the sum kept so far, e^(m_old - m_new) (0 before anything was kept) --
+    the rescale of "The identity" (first page).  Blocks with no finite score
+    leave the state unchanged and produce no entry.  Returns a list of
+    (m, l, factor).
+    """
+    state = (_NEG_INF, 0.0, None)
     trace = []
     for blk in blocks:
-        blk = np.asarray(blk, dtype=np.float64)
-        if blk.size == 0:
+        b = _block_state(np.asarray(blk, dtype=np.float64).ravel()[None, :])
+        if np.isneginf(b[0][0]):
             continue
-        bmax = float(blk.max())
-        if bmax == _NEG_INF:
-            continue
-        m_new = max(m, bmax)
-        factor = 0.0 if m == _NEG_INF else math.exp(m - m_new)
-        l = l * factor + float(np.exp(blk - m_new).sum())
-        m = m_new
-        trace.append((m, l, factor))
+        m_old = state[0]
+        m, l, _ = _merge(state, (b[0][0], b[1][0], None))
+        factor = 0.0 if m_old == _NEG_INF else math.exp(m_old - m)
+        state = (float(m), float(l), None)
+        trace.append((state[0], state[1], factor))
     return trace
 
 
-def streaming_logsumexp(x, block=7):
-    """log(sum(exp(x))) in one pass over blocks of ``block`` values.
+def logsumexp_by_blocks(x, block_size=16):
+    """ln(sum_j e^(x_j)) of a 1-D array, reading it block_size values at a time.
 
-    Uses online_normalizer_trace; an input with no finite value returns -inf
-    rather than log(0) ("The identity", first page).
+    Each block's (max, sum) is merged into the running one (see _merge); an
+    input with no finite value gives -inf rather than the log of 0 ("The
+    identity", first page).
     """
     x = np.asarray(x, dtype=np.float64).ravel()
-    trace = online_normalizer_trace(x[i:i + block] for i in range(0, x.size, block))
-    if not trace or trace[-1][1] == 0.0:
-        return _NEG_INF
-    m, l, _ = trace[-1]
-    return m + math.log(l)
+    state = (_NEG_INF, 0.0, None)
+    for a in range(0, x.size, block_size):
+        b = _block_state(x[a:a + block_size][None, :])
+        state = _merge(state, (b[0][0], b[1][0], None))
+    m, l = float(state[0]), float(state[1])
+    return _NEG_INF if l == 0.0 else m + math.log(l)
 
 
-def tiled_forward(q, k, v, scale, causal=False, block_q=32, block_k=32):
-    """The blocked recurrence of "From softmax to attention" (first page).
+def tiled_forward(q, k, v, scale, causal=False, block_q=16, block_k=16):
+    """The blocked form of attention of "From softmax to attention" (first page).
 
-    For each block of query rows, three running quantities start at
-    m = -inf, l = 0 and an unnormalised output of zeros.  Each key/value block
-    visited (in increasing key order) gives a score tile S; with
-    m_new = max(m, rowmax S) and factor a = e^(m - m_new) (0 while m is -inf),
-    the update is l <- a*l + rowsum(e^(S - m_new)), O <- a*O + e^(S - m_new) V,
-    m <- m_new.  The division by l happens once, after the last block, and
-    L = m + ln(l).  With the causal mask, a key block that starts after the
-    last query of the query block is never visited, nor is any later one.
-
-    Returns (O, L, tiles) where ``tiles`` counts the score tiles computed.
-    The largest query-by-key array built is one block_q x block_k tile.
+    Queries are cut into blocks of block_q rows and keys into blocks of
+    block_k.  Every (query block, key block) score tile yields one partial
+    state per row, merged into the row's running state by the identity of
+    _merge, in increasing key order; the division by l happens once, at the
+    end, and L = m + ln l.  With the causal mask ("Causal masking", first
+    page) a key block whose first key comes after the block's last query is
+    never formed -- every score in it would be -inf.  Returns (O, L, tiles);
+    the largest query-by-key array built is one tile.
     """
     q = _as2d(q, "Q")
     k = _as2d(k, "K")
     v = _as2d(v, "V")
-    if block_q < 1 or block_k < 1:
-        raise ValueError("block sizes must be positive")
+    if block_q <= 0 or block_k <= 0:
+        raise ValueError("tile sides must be at least 1")
     tq, tk, dv = q.shape[0], k.shape[0], v.shape[1]
-    o = np.zeros((tq, dv), dtype=np.float64)
+    out = np.zeros((tq, dv), dtype=np.float64)
     lse = np.full((tq,), _NEG_INF, dtype=np.float64)
     tiles = 0
-    if tk == 0:
-        return o, lse, tiles
-    for q0 in range(0, tq, block_q):
-        qi = np.arange(q0, min(tq, q0 + block_q))
-        run_m = np.full((qi.size,), _NEG_INF)
-        run_l = np.zeros((qi.size,))
-        acc = np.zeros((qi.size, dv))
-        for k0 in range(0, tk, block_k):
-            if causal and k0 > qi[-1]:
-                break
-            kj = slice(k0, min(tk, k0 + block_k))
-            s = (q[qi] @ k[kj].T) * scale
+    for r0 in range(0, tq, block_q):
+        rows = np.arange(r0, min(tq, r0 + block_q))
+        starts = [c0 for c0 in range(0, tk, block_k) if not (causal and c0 > rows[-1])]
+        state = (np.full(rows.size, _NEG_INF), np.zeros(rows.size), np.zeros((rows.size, dv)))
+        for c0 in starts:
+            cols = np.arange(c0, min(tk, c0 + block_k))
+            x = _scores(q[rows], rows, k[cols], scale, False)
             if causal:
-                key_pos = np.arange(kj.start, kj.stop)[None, :]
-                s = np.where(key_pos > qi[:, None], _NEG_INF, s)
+                x = np.where(cols[None, :] > rows[:, None], _NEG_INF, x)
+            state = _merge(state, _block_state(x, v[cols]))
             tiles += 1
-            m_new = np.maximum(run_m, s.max(axis=1))
-            # rows whose max is still -inf have seen no visible key yet: shift by 0
-            shift = np.where(np.isneginf(m_new), 0.0, m_new)
-            factor = np.where(np.isneginf(run_m), 0.0, np.exp(run_m - shift))
-            e = np.exp(s - shift[:, None])
-            run_l = factor * run_l + e.sum(axis=1)
-            acc = factor[:, None] * acc + e @ v[kj]
-            run_m = m_new
-        o[qi] = acc / run_l[:, None]
-        lse[qi] = run_m + np.log(run_l)
-    return o, lse, tiles
+        m, l, o = state
+        seen = l > 0
+        out[rows] = np.where(seen[:, None], o / np.where(seen, l, 1.0)[:, None], 0.0)
+        with np.errstate(divide="ignore"):
+            lse[rows] = np.where(seen, m + np.log(np.where(seen, l, 1.0)), _NEG_INF)
+    return out, lse, tiles

@@ -5,9 +5,9 @@ path imports this module, and it shares no code with the HIP library.
 
 Source: "Why FlashAttention Can Avoid a Square Attention Array Without Making
 Attention Linear" (leviathansystems.co), section "Backward can recreate tiles
-instead of retaining the square": with dropout enabled, the algorithm keeps the
-state of its pseudorandom generator and rebuilds the same dropout mask during
-the backward pass rather than storing a square mask.  The pages name no
+instead of retaining the square": under dropout, only the generator state is
+kept from the forward, and the backward regenerates the identical mask from it,
+so no N x N mask is ever stored.  The pages name no
 generator, no mask layout and no rescaling rule; the choices below are this
 implementation's reading and are stated once here.
 

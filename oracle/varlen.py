@@ -5,11 +5,11 @@ TEST INFRASTRUCTURE ONLY (see the package docstring): nothing on the product
 path imports this module, and it shares no code with the HIP library.
 
 Source: "FlashAttention: The Matrix You Never Have to Write Down"
-(maitreyasuin.github.io), the PyTorch-API notes ("Padding is silent waste"):
-padding every sequence to the longest one makes a fused kernel do work for
-the padded positions, and at mixed lengths packing or a variable-length
-kernel matters more than the attention implementation.  The page fixes no
-layout; this implementation's reading:
+(maitreyasuin.github.io), the tips on PyTorch calls under "What it doesn't
+solve": when every sequence of a batch is padded to the longest, a fused
+kernel still spends work on the padded positions, so for batches of mixed
+lengths the page recommends packing the sequences (or a kernel that takes
+variable lengths).  The page fixes no layout; this implementation's reading:
 
   * Q, K, V are [H, total, d] (head-major): sequence b occupies rows
     cu[b] .. cu[b+1]-1 of every head, with cu non-decreasing, cu[0] = 0 and

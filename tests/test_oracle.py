@@ -55,7 +55,7 @@ def test_four_number_online_example():
     dense = sum(math.exp(x - 10.0) for blk in g["blocks"] for x in blk)
     assert f"{dense:.6f}" == g["dense_sum_6dp"]
     assert abs(l2 - dense) <= 1e-15
-    assert abs(oracle.streaming_logsumexp([1.0, 2.0, 10.0, 0.0], block=2) - (10.0 + math.log(dense))) <= 1e-15
+    assert abs(oracle.logsumexp_by_blocks([1.0, 2.0, 10.0, 0.0], block_size=2) - (10.0 + math.log(dense))) <= 1e-15
 
 
 def test_late_max_in_final_key_tile():
@@ -69,21 +69,21 @@ def test_late_max_in_final_key_tile():
     assert f"{ot[0, 0]:.7f}" == g["printed_7dp"]
 
 
-def test_streaming_logsumexp_guards_and_seeded_example():
+def test_blockwise_logsumexp_guards_and_seeded_example():
     g = GOLDEN["streaming_lse"]
-    assert oracle.streaming_logsumexp(np.full(4, -np.inf)) == -np.inf
-    assert oracle.streaming_logsumexp(np.array([])) == -np.inf
+    assert oracle.logsumexp_by_blocks(np.full(4, -np.inf)) == -np.inf
+    assert oracle.logsumexp_by_blocks(np.array([])) == -np.inf
     # a block of pure -inf in the middle is skipped, not turned into NaN
     x = np.array([-np.inf, -np.inf, 1.0, 2.0, -np.inf, -np.inf, 0.5])
     want = math.log(math.exp(1.0) + math.exp(2.0) + math.exp(0.5))
-    assert abs(oracle.streaming_logsumexp(x, block=2) - want) <= 1e-14
+    assert abs(oracle.logsumexp_by_blocks(x, block_size=2) - want) <= 1e-14
     torch.manual_seed(g["torch_manual_seed"])
     xs = (torch.randn(g["count"]) * g["multiplier"]).double().numpy()
-    got = oracle.streaming_logsumexp(xs, block=g["block"])
+    got = oracle.logsumexp_by_blocks(xs, block_size=g["block"])
     assert f"{got:.8f}" == g["streaming_printed_8dp"]
     assert abs(got - float(g["dense_fp32_printed_8dp"])) < g["page_tolerance"]
     for blk in (1, 3, 64, 1000, 4096):
-        assert abs(oracle.streaming_logsumexp(xs, block=blk) - got) <= 1e-12
+        assert abs(oracle.logsumexp_by_blocks(xs, block_size=blk) - got) <= 1e-12
 
 
 # --------------------------------------------------------------------- closed forms and brute force
@@ -181,15 +181,17 @@ def test_empty_key_sequence_policy():
 def test_tiled_equals_one_shot_on_ragged_blocks():
     g = GOLDEN["tiled_vs_dense_sweep"]
     rng = np.random.default_rng(16)
+    # upper-left causal masking is defined for any (Tq, Tk), so every shape
+    # runs both ways, with every tile shape of the fixture
+    cases = [(shape, causal, blocks) for shape in g["shapes_tq_tk_d_dv"] for causal in (False, True)
+             for blocks in g["blocks_q_k"]]
     worst = 0.0
-    for tq, tk, d, dv in g["shapes_tq_tk_d_dv"]:
-        for causal in ([False, True] if tq == tk else [False]):
-            for bq, bk in g["blocks_q_k"]:
-                q, k, v = rng.normal(size=(tq, d)), rng.normal(size=(tk, d)), rng.normal(size=(tk, dv))
-                scale = 1 / math.sqrt(d)
-                o, l, _ = oracle.tiled_forward(q, k, v, scale, causal, bq, bk)
-                oe, le = oracle.attention_forward(q, k, v, scale, causal)
-                worst = max(worst, np.max(np.abs(o - oe)), np.max(np.abs(l - le)))
+    for (tq, tk, d, dv), causal, (bq, bk) in cases:
+        q, k, v = rng.normal(size=(tq, d)), rng.normal(size=(tk, d)), rng.normal(size=(tk, dv))
+        scale = 1 / math.sqrt(d)
+        o, l, _ = oracle.tiled_forward(q, k, v, scale, causal, bq, bk)
+        oe, le = oracle.attention_forward(q, k, v, scale, causal)
+        worst = max(worst, np.max(np.abs(o - oe)), np.max(np.abs(l - le)))
     assert worst <= 1e-12
 
 
