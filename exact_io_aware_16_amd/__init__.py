@@ -19,7 +19,7 @@ import os
 import torch
 
 __all__ = ["forward", "forward_splitkv", "backward", "backward_prep", "backward_dkdv", "backward_dq",
-           "forward_dropout", "backward_dropout", "forward_varlen", "backward_varlen", "workspace_for",
+           "forward_dropout", "backward_dropout", "dropout_applied_p", "forward_varlen", "backward_varlen", "workspace_for",
            "library", "FAError", "LIB_PATH", "status_string"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -76,6 +76,8 @@ def library():
         i64p = ctypes.POINTER(ctypes.c_int64)
         lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, f, i, vp]
         lib.fa_fwd_strided.restype = i
+        lib.fa_dropout_applied_p.argtypes = [f]
+        lib.fa_dropout_applied_p.restype = f
         lib.fa_status_string.argtypes = [i]
         lib.fa_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -86,44 +88,43 @@ def status_string(status):
     return library().fa_status_string(int(status)).decode()
 
 
-def _check(q, k, v, square=True, strided=False):
-    """Input contract: the page's single-head checks, extended to [B, H, N, d].
+_KERNEL_DTYPES = (torch.bfloat16, torch.float32)
 
-    square=False admits the page's general shapes, Q [B,H,Nq,d], K [B,H,Nk,d],
-    V [B,H,Nk,dv]; square=True also requires Nq == Nk and dv == d.
-    strided=True admits views whose head-dim stride is 1 (the others may be
-    anything the strided forward accepts).
+
+def _check(q, k, v, square=True, strided=False):
+    """Host-side check of the inputs against the C ABI (include/fa.h).
+
+    The rules are listed once, in the order they are tested; the first one
+    broken raises.  square=False admits the general shapes of fa_fwd_ex
+    (Q [B,H,Nq,d], K [B,H,Nk,d], V [B,H,Nk,dv]); strided=True admits views
+    with a unit head-dim stride (fa_fwd_strided).  Head widths outside the
+    kernels' set come back from the library as FA_ERR_HEADDIM.
     """
-    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
-        raise ValueError("Q, K, V must be rank 4 [B, H, N, d]")
-    if not all(t.is_floating_point() for t in (q, k, v)):
-        raise TypeError("Q, K, V must be floating point")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError(f"dtypes differ: {q.dtype}, {k.dtype}, {v.dtype}")
-    if q.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError(f"unsupported dtype {q.dtype} (bfloat16 or float32)")
-    if k.shape[-1] != q.shape[-1]:
-        raise ValueError(f"Q and K widths differ: {q.shape[-1]} vs {k.shape[-1]}")
-    if v.shape[-2] != k.shape[-2]:
-        raise ValueError(f"K and V lengths differ: {k.shape[-2]} vs {v.shape[-2]}")
-    if q.shape[-1] == 0:
-        raise ValueError("query/key width must be positive")
-    if not (q.device == k.device == v.device):
-        raise ValueError("Q, K, V must be on the same device")
-    if q.shape[:2] != k.shape[:2] or k.shape[:2] != v.shape[:2]:
-        raise ValueError(f"batch and head counts differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
-    if v.shape[-1] == 0:
-        raise ValueError("value width must be positive")
-    if square and (q.shape != k.shape or k.shape != v.shape):
-        raise ValueError(f"Q, K, V must share one [B, H, N, d] shape, got {tuple(q.shape)}, "
-                         f"{tuple(k.shape)}, {tuple(v.shape)}")
-    if strided:
-        if any(t.stride(-1) != 1 for t in (q, k, v)):
-            raise ValueError("Q, K, V must have unit stride along the head dimension")
-    elif not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("Q, K, V must be contiguous")
-    if q.device.type != "cuda":
-        raise ValueError("Q, K, V must be GPU tensors")
+    shapes = lambda: f"q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}"
+    rules = (
+        (lambda: q.dim() == k.dim() == v.dim() == 4, ValueError,
+         lambda: f"q, k, v: expected 4-D [batch, heads, rows, width] tensors, got {shapes()}"),
+        (lambda: q.dtype == k.dtype == v.dtype and q.dtype in _KERNEL_DTYPES, TypeError,
+         lambda: f"q, k, v: one dtype, bfloat16 (or float32 for the float32 kernel), got "
+                 f"{q.dtype}, {k.dtype}, {v.dtype}"),
+        (lambda: q.shape[:2] == k.shape[:2] == v.shape[:2], ValueError,
+         lambda: f"q, k, v: batch and head counts must agree, got {shapes()}"),
+        (lambda: q.shape[3] == k.shape[3] and q.shape[3] > 0 and v.shape[3] > 0, ValueError,
+         lambda: f"score width: q and k need one positive width d (and v a positive width), got {shapes()}"),
+        (lambda: k.shape[2] == v.shape[2], ValueError,
+         lambda: f"key count: k and v need the same number of rows, got {shapes()}"),
+        (lambda: not square or q.shape == k.shape == v.shape, ValueError,
+         lambda: f"this entry point takes one shared [B, H, N, d] shape, got {shapes()}"),
+        (lambda: (all(t.stride(-1) == 1 for t in (q, k, v)) if strided
+                  else all(t.is_contiguous() for t in (q, k, v))), ValueError,
+         lambda: ("q, k, v: views need unit stride along the head dimension" if strided
+                  else "q, k, v: this entry point takes contiguous tensors")),
+        (lambda: q.device == k.device == v.device and q.device.type == "cuda", ValueError,
+         lambda: f"q, k, v: all on one GPU (the kernels have no CPU path), got {q.device}, {k.device}, {v.device}"),
+    )
+    for ok, exc, message in rules:
+        if not ok():
+            raise exc(message())
 
 
 def _ptr(t):
@@ -273,12 +274,22 @@ def _dropout_args(p, seed, offset):
     return p, seed, offset
 
 
+def dropout_applied_p(p):
+    """The dropout probability the kernels apply for a requested ``p``
+    (fa_dropout_applied_p): p is quantised to t / 256 with
+    t = min(255, round(256 p)), e.g. 0.1 -> 26/256 = 0.1015625."""
+    p, _, _ = _dropout_args(p, 0, 0)
+    return float(library().fa_dropout_applied_p(p))
+
+
 def forward_dropout(q, k, v, p, seed, offset=0, causal=False, scale=None, out=None, lse=None):
     """forward() with dropout on the normalised weights (fa_fwd_dropout).
 
     The mask is a function of (seed, offset, head, row, key) only, so
     backward_dropout with the same arguments regenerates it.  bf16 inputs of
     one shared [B,H,N,d] shape; L is the logsumexp without dropout.
+    Returns (O, L, p_applied): the probability actually applied, p quantised
+    to a multiple of 1/256 (see dropout_applied_p).
     """
     if q.dtype != torch.bfloat16:
         raise TypeError("dropout takes bfloat16 Q, K, V")
@@ -290,7 +301,7 @@ def forward_dropout(q, k, v, p, seed, offset=0, causal=False, scale=None, out=No
                                   int(bool(causal)), p, seed, offset, _stream(q.device))
     if st != FA_OK:
         raise FAError("fa_fwd_dropout", st)
-    return o, l
+    return o, l, dropout_applied_p(p)
 
 
 def backward_dropout(q, k, v, o, lse, do, p, seed, offset=0, causal=False, scale=None, workspace=None):
@@ -331,6 +342,14 @@ def _check_varlen(q, k, v, cu_seqlens, max_seqlen):
     return max_seqlen
 
 
+def _dense_on(device, **tensors):
+    """The kernels address these buffers as dense arrays from their data
+    pointer: each must be contiguous and on the inputs' device."""
+    for name, t in tensors.items():
+        if not t.is_contiguous() or t.device != device:
+            raise ValueError(f"{name} must be a contiguous tensor on {device}")
+
+
 def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, out=None, lse=None):
     """Attention over packed variable-length sequences (fa_fwd_varlen).
 
@@ -346,6 +365,7 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, ou
     l = lse if lse is not None else torch.empty((H, total), dtype=torch.float32, device=q.device)
     if o.shape != (H, total, d) or l.shape != (H, total) or o.dtype != torch.float32 or l.dtype != torch.float32:
         raise ValueError("out must be float32 [H, total, d] and lse float32 [H, total]")
+    _dense_on(q.device, out=o, lse=l)
     st = library().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), _ptr(cu_seqlens), B, H, total,
                                  max_seqlen, d, _scale(scale, d), int(bool(causal)), _stream(q.device))
     if st != FA_OK:
@@ -360,8 +380,8 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, s
     max_seqlen = _check_varlen(q, k, v, cu_seqlens, max_seqlen)
     H, total, d = q.shape
     B = cu_seqlens.numel() - 1
-    if do.dtype != torch.bfloat16 or do.shape != q.shape or not do.is_contiguous():
-        raise ValueError("dO must be a contiguous bfloat16 tensor of Q's shape")
+    if do.dtype != torch.bfloat16 or do.shape != q.shape:
+        raise ValueError("dO must be a bfloat16 tensor of Q's shape")
     if o.dtype != torch.float32 or o.shape != q.shape or lse.dtype != torch.float32 or lse.shape != (H, total):
         raise ValueError("O and L must be the float32 outputs of forward_varlen")
     ws_bytes = library().fa_bwd_workspace_bytes(1, H, total, d)
@@ -369,6 +389,7 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, s
         workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < ws_bytes:
         raise ValueError(f"workspace too small: need {ws_bytes} bytes")
+    _dense_on(q.device, dO=do, O=o, L=lse, workspace=workspace)
     dq = torch.empty((H, total, d), dtype=torch.float32, device=q.device)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)

@@ -73,7 +73,18 @@ int check_strides(const void* p, const int64_t* st, int n_rows, int width) {
   return FA_OK;
 }
 
-int check_scale(float scale) { return (std::isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_SCALE; }
+// Any finite scale is accepted: 0 gives uniform weights over the visible
+// keys, a negative scale reverses the order of the scores.
+int check_scale(float scale) { return std::isfinite(scale) ? FA_OK : FA_ERR_SCALE; }
+
+// The forward kernels mark hidden keys with -inf scores before multiplying
+// by the scale, which for scale 0 would give 0 * -inf.  Scale 0 therefore
+// runs as 2^-100: every visible score then differs from the row reference by
+// less than 2^-80 in log2 units, and its float32 weight 2^(that) rounds to 1,
+// which is the uniform weighting scale 0 defines (L = ln of the visible
+// count up to about 1e-28).  The backward masks after the exponential and
+// takes the scale as given.
+float forward_scale(float scale) { return scale == 0.f ? 0x1p-100f : scale; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
@@ -98,6 +109,13 @@ int make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* out, bool
 
 extern "C" {
 
+float fa_dropout_applied_p(float p_drop) {
+  fa::Dropout dp{};
+  bool active = false;
+  if (make_dropout(p_drop, 0, 0, &dp, &active) != FA_OK) return -1.f;
+  return (float)dp.t / 256.f;
+}
+
 int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, hipStream_t stream) {
   bool empty = false;
@@ -107,7 +125,8 @@ int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, in
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   return hip_status(
-      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, scale, nullptr, nullptr, stream));
+      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, forward_scale(scale), nullptr,
+                          nullptr, stream));
 }
 
 int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int d,
@@ -120,8 +139,8 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float*
   if ((st = make_dropout(p_drop, seed, offset, &dp, &active)) != FA_OK) return st;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr, scale,
-                                        active ? &dp : nullptr, nullptr, stream));
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, N, d, d, causal, 1, nullptr,
+                                        forward_scale(scale), active ? &dp : nullptr, nullptr, stream));
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int Nq, int Nk, int d,
@@ -133,7 +152,8 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,
   if (empty) return FA_OK;
   if (!o || !lse || (Nk > 0 && (!q || !k || !v))) return FA_ERR_NULL;
   return hip_status(
-      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, scale, nullptr, nullptr, stream));
+      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, forward_scale(scale), nullptr,
+                          nullptr, stream));
 }
 
 int fa_fwd_strided(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int Nq, int Nk,
@@ -150,8 +170,8 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, float* o, float*
   if (!o || !lse || (Nk > 0 && (!q || !k || !v))) return FA_ERR_NULL;
   const fa::Strides lay{q_strides[0], q_strides[1], k_strides[0], k_strides[1], v_strides[0], v_strides[1],
                         (int)q_strides[2],  (int)k_strides[2],  (int)v_strides[2],  H};
-  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr, scale, nullptr,
-                                        nullptr, stream, &lay));
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, 1, nullptr,
+                                        forward_scale(scale), nullptr, nullptr, stream, &lay));
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dv, int n_splits) {
@@ -175,7 +195,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float*
   const int n = fa::fwd_splitkv_resolve(B * H, Nq, Nk, d, dv, n_splits);
   if (n > 1 && !workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, Nq, Nk, d, dv, causal, n,
-                                        static_cast<float*>(workspace), scale, nullptr, nullptr, stream));
+                                        static_cast<float*>(workspace), forward_scale(scale), nullptr, nullptr, stream));
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
@@ -186,7 +206,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (empty) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  return hip_status(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, scale, causal, stream));
+  return hip_status(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, forward_scale(scale), causal, stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -275,7 +295,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* 
   if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
   const fa::Seqs sq{cu_seqlens, H, total};
   return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, max_seqlen, max_seqlen, d, d, causal, 1, nullptr,
-                                        scale, nullptr, &sq, stream));
+                                        forward_scale(scale), nullptr, &sq, stream));
 }
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
@@ -299,7 +319,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (negative B/H/N, causal not 0/1, or size overflow)";
     case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
-    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_WORKSPACE: return "workspace is NULL";
     case FA_ERR_HIP: return "HIP runtime rejected a kernel launch";
     case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1)";

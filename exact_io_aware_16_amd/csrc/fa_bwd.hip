@@ -1,10 +1,10 @@
 // Exact attention backward by recomputation, bf16 inputs, float32 gradients.
 //
-// The pages keep Q, K, V, O and the per-row logsumexp L from the forward and
-// rebuild the score and probability tiles when the gradients need them ("The
-// forward pass is only half of it", FlashAttention: The Matrix You Never
-// Have to Write Down; "Backward can recreate tiles instead of retaining the
-// square", leviathansystems.co).  They give no gradient formulas; the
+// Per the pages, the forward saves only Q, K, V, O and the per-row
+// logsumexp L, and the backward recomputes every score / probability tile it
+// needs from them ("The forward pass is only half of it", FlashAttention:
+// The Matrix You Never Have to Write Down; "Backward can recreate tiles
+// instead of retaining the square", leviathansystems.co).  They give no gradient formulas; the
 // kernels use the chain rule on softmax(scale Q K^T) V:
 //   P = exp(scale S - L),  dV = P^T dO,  dP = dO V^T,
 //   D_i = sum_j P_ij dP_ij = dO_i . O_i,  dS = P * (dP - D),

@@ -311,11 +311,22 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
     vaddr[db] = kr * DV * 2 + 16 * ((d >> 3) ^ vswz<DV>(kr)) + 2 * (d & 7);
   }
 
+  // A negative scale is folded into Q (a bf16 sign flip is exact), so the
+  // scores' row max times c = |scale| log2(e) is the max of the scaled row.
   bf16x8 qf[NKK];
   {
     const int qr = min(my_q, Nq - 1);
+    const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(ld16(Qh + (size_t)qr * q_stride + 16 * kk + 8 * g));
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 x = ld16(Qh + (size_t)qr * q_stride + 16 * kk + 8 * g);
+      x.x ^= qsign;
+      x.y ^= qsign;
+      x.z ^= qsign;
+      x.w ^= qsign;
+      qf[kk] = as_bf16x8(x);
+    }
+    c = fabsf(c);
   }
 
   f32x16 oacc[NDB];

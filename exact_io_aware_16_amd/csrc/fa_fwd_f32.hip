@@ -68,23 +68,25 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 #pragma unroll
       for (int j = 0; j < NK; ++j) s[j] = fmaf(qv, sm.k[4 * j + p][cc], s[j]);
     }
+    // scores in log2 units (scaled before the max, so any sign of the scale
+    // works), masked ones -inf
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int key = key0 + 4 * j + p;
-      if (key >= N || (CAUSAL && key > my_q)) s[j] = -INFINITY;
+      s[j] = (key >= N || (CAUSAL && key > my_q)) ? -INFINITY : s[j] * c;
       mx = fmaxf(mx, s[j]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 1));
     mx = fmaxf(mx, __shfl_xor(mx, 2));
-    const float m_new = fmaxf(m_run, mx * c);
+    const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_use);
     m_run = m_new;
     float rs = 0.f;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-      const float pv = exp2f(fmaf(s[j], c, -m_use));
+      const float pv = exp2f(s[j] - m_use);
       rs += pv;
       sm.p[r][4 * j + p] = pv;
     }

@@ -53,7 +53,7 @@ typedef enum {
                            INT32_MAX, or N*d*4 above INT32_MAX (one head of a
                            float32 tensor must be byte-addressable in 31 bits) */
   FA_ERR_HEADDIM = 3,   /* d is not a supported head width (64 or 128)         */
-  FA_ERR_SCALE = 4,     /* scale is not finite and > 0                         */
+  FA_ERR_SCALE = 4,     /* scale is not finite (inf or NaN)                    */
   FA_ERR_WORKSPACE = 5, /* a required workspace is NULL                        */
   FA_ERR_HIP = 6,       /* a kernel launch was rejected by the HIP runtime     */
   FA_ERR_DROPOUT = 7    /* dropout probability not in [0, 1)                   */
@@ -65,7 +65,11 @@ typedef enum {
  *   o       : device, float32 [B,H,N,d]  -- normalised output
  *   lse     : device, float32 [B,H,N]    -- per-row logsumexp of the scaled,
  *             masked scores, natural log; the statistic the backward needs
- *   d       : 64 or 128;  scale > 0 and finite (usually 1/sqrt(d))
+ *   d       : 64 or 128
+ *   scale   : any finite value, usually 1/sqrt(d) ("Build it" fixes that
+ *             choice; the caller may pass another).  0 weighs every visible
+ *             key equally (O = their mean, L = ln of their count); a negative
+ *             scale reverses the order of the scores.
  * Scores and their running max/sum stay on chip: S = Q K^T is formed one
  * key tile at a time on bf16 matrix cores with float32 accumulation, the
  * probabilities are rounded to bf16 for the P V product, and O is divided by
@@ -129,7 +133,9 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float*
 
 /*
  * Forward pass with float32 inputs, computed entirely in float32 (same
- * contract as fa_fwd otherwise).  For small exact checks; not tuned.
+ * contract as fa_fwd otherwise): the precision of the first page's own
+ * exactness check ("Check it", float32 against a float64 reference at
+ * 1e-5).  For small exact checks; not tuned.
  */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
@@ -137,7 +143,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 /*
  * Bytes of device workspace fa_bwd needs: two float32 per query row
  * (scale * D_i with D_i = dO_i . O_i, and L_i log2(e)).  Returns 0 for an
- * empty or invalid shape.
+ * empty or invalid shape.  Infrastructure (buffer sizing): no passage of the
+ * pages defines it; D_i is the row sum of the chain-rule backward that
+ * fa_bwd documents.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -178,6 +186,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const fl
  * same p_drop, seed and offset gives the gradients of that O; the workspace
  * is fa_bwd_workspace_bytes.  p_drop = 0 runs the plain kernels.
  */
+/* The dropout probability the two calls above apply for p_drop: the
+ * generator bytes are compared with t = min(255, round(256 p_drop)), so the
+ * applied probability is t / 256 (p_drop = 0.1 applies 26/256 = 0.1015625).
+ * Returns -1 for a p_drop outside [0, 1). */
+float fa_dropout_applied_p(float p_drop);
 int fa_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse,
                    int B, int H, int N, int d, float scale, int causal,
                    float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream);
@@ -188,8 +201,9 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, 
 
 /*
  * Packed variable-length sequences: instead of padding every sequence to the
- * longest one, sequences share one token axis ("Padding is silent waste",
- * FlashAttention: The Matrix You Never Have to Write Down, PyTorch API notes).
+ * longest one, sequences share one token axis (the padding note among the
+ * tips on PyTorch calls under "What it doesn't solve", FlashAttention: The
+ * Matrix You Never Have to Write Down: padded positions cost work).
  *   q, k, v    : device, bf16 [H, total, d] head-major; sequence b occupies
  *                rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head
  *   o          : device, float32 [H, total, d];  lse : float32 [H, total]
@@ -237,7 +251,8 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const void* workspace,
               float* dq, int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
-/* Static, human-readable text for an fa_status value (never NULL). */
+/* Static, human-readable text for an fa_status value (never NULL).
+ * Infrastructure (error reporting): no passage of the pages defines it. */
 const char* fa_status_string(int status);
 
 #ifdef __cplusplus

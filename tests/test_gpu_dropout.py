@@ -3,7 +3,8 @@ the float64 dropout oracle.  The mask is regenerated from (seed, offset) by
 the forward and by both backward kernels ("Backward can recreate tiles instead
 of retaining the square", second page), so the gradients only match when all
 three kernels rebuild the same mask the oracle draws.  Tolerances as in
-test_gpu_parity: O max-abs 1e-2 / relative L2 5e-3, gradients 2e-2 / 2e-2,
+test_gpu_parity: O max-abs 1e-2 / relative L2 5e-3, gradients 1e-2 / 2e-2
+(the max-abs gate scaled by the keep factor 1/(1-p), see gmax),
 L 1e-3.
 """
 
@@ -22,8 +23,19 @@ from oracle import dropout as Dr
 pytestmark = pytest.mark.gpu
 
 O_MAX, O_REL = 1e-2, 5e-3
-G_MAX, G_REL = 2e-2, 2e-2
+G_MAX, G_REL = 1e-2, 2e-2
 L_MAX = 1e-3
+
+
+def gmax(p):
+    """Max-abs gate of the gradients under dropout.  Kept weights are
+    multiplied by r = 256 / (256 - t) (t / 256 the applied probability), and
+    so are O, dV and the dropout terms of dS: the absolute error of the
+    bf16-rounded weights scales with r while the relative error does not.
+    The absolute gate is therefore G_MAX * r (relative L2 stays G_REL); r = 1
+    without dropout."""
+    t = min(255, int(math.floor(256 * p + 0.5)))
+    return G_MAX * 256 / (256 - t)
 
 
 def say(msg):
@@ -70,7 +82,8 @@ def test_dropout_forward_and_backward(B, H, N, d, causal, p):
     scale = 1 / math.sqrt(d)
     say(f"dropout B={B} H={H} N={N} d={d} causal={causal} p={p}")
     q, k, v, do = gpu(t, "q", "k", "v", "do")
-    o, l = fa.forward_dropout(q, k, v, p, seed, offset, causal=causal)
+    o, l, p_applied = fa.forward_dropout(q, k, v, p, seed, offset, causal=causal)
+    assert p_applied == round(256 * p) / 256
     dq, dk, dv = fa.backward_dropout(q, k, v, o, l, do, p, seed, offset, causal=causal)
     torch.cuda.synchronize()
     q64, k64, v64, do64 = (I.to_f64(t[n]) for n in ("q", "k", "v", "do"))
@@ -83,7 +96,7 @@ def test_dropout_forward_and_backward(B, H, N, d, causal, p):
     for name, x, ref in (("dQ", dq, gref[0]), ("dK", dk, gref[1]), ("dV", dv, gref[2])):
         ge, gr = errs(x.cpu().numpy(), ref)
         say(f"  {name} max-abs {ge:.3e} rel-L2 {gr:.3e}")
-        assert ge <= G_MAX and gr <= G_REL, name
+        assert ge <= gmax(p) and gr <= G_REL, name
 
 
 def test_dropout_in_the_large_grid_launch():
@@ -93,7 +106,7 @@ def test_dropout_in_the_large_grid_launch():
     t = inputs(B, H, N, d, 951)
     q, k, v, do = gpu(t, "q", "k", "v", "do")
     say("dropout large grid B=4 H=16 N=1024 d=128 causal")
-    o, l = fa.forward_dropout(q, k, v, p, seed, 0, causal=True)
+    o, l, _ = fa.forward_dropout(q, k, v, p, seed, 0, causal=True)
     dq, dk, dv = fa.backward_dropout(q, k, v, o, l, do, p, seed, 0, causal=True)
     torch.cuda.synchronize()
     scale = 1 / math.sqrt(d)
@@ -108,7 +121,7 @@ def test_dropout_in_the_large_grid_launch():
         gref = Dr.attention_backward_dropout(q64, k64, v64, do64, scale, True, keep, t_)
         for name, x, ref in (("dQ", dq, gref[0]), ("dK", dk, gref[1]), ("dV", dv, gref[2])):
             ge, gr = errs(x[b, h].cpu().numpy(), ref)
-            assert ge <= G_MAX and gr <= G_REL, (name, b, h)
+            assert ge <= gmax(p) and gr <= G_REL, (name, b, h)
         say(f"  head ({b},{h}) O max-abs {me:.3e}")
 
 
@@ -116,7 +129,8 @@ def test_dropout_zero_probability_is_the_plain_path():
     t = inputs(1, 2, 300, 128, 961)
     q, k, v, do = gpu(t, "q", "k", "v", "do")
     o0, l0 = fa.forward(q, k, v, causal=True)
-    o1, l1 = fa.forward_dropout(q, k, v, 0.0, 77, causal=True)
+    o1, l1, p0 = fa.forward_dropout(q, k, v, 0.0, 77, causal=True)
+    assert p0 == 0.0
     g0 = fa.backward(q, k, v, o0, l0, do, causal=True)
     g1 = fa.backward_dropout(q, k, v, o1, l1, do, 0.0, 77, causal=True)
     torch.cuda.synchronize()

@@ -3,7 +3,8 @@
 Inputs are the seeded bf16/fp32 draws of exact_io_aware_16_amd.inputs; the
 oracle sees the exact stored values in float64.  Tolerances (floating point):
   O:           max-abs <= 1e-2 and relative L2 <= 5e-3
-  dQ, dK, dV:  max-abs <= 2e-2 and relative L2 <= 2e-2
+  dQ, dK, dV:  max-abs <= 1e-2 and relative L2 <= 2e-2 (the 2e-2 stated for
+               the gradients bounds the relative L2; max-abs keeps 1e-2)
   L (logsumexp, our reading, no stated bound): max-abs <= 1e-3
 The float32 path is held to the first page's own bar, 1e-5.
 """
@@ -23,7 +24,7 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 O_MAX, O_REL = 1e-2, 5e-3
-G_MAX, G_REL = 2e-2, 2e-2
+G_MAX, G_REL = 1e-2, 2e-2
 L_MAX = 1e-3
 
 
@@ -274,9 +275,47 @@ def test_fwd_4k_d128_full():
     check_fwd(o, l, oref, lref, w.name)
 
 
-@pytest.mark.parametrize("w", [I.CAUSAL_8K_D64_WIDE, I.CAUSAL_32K_D128], ids=lambda w: w.name)
+@pytest.fixture(scope="module")
+def wide_scores_run():
+    """The wide-score causal workload (B4 H16 N8192 d64, Q and K ~ N(0, 3^2))
+    run once at full size; its outputs are compared part by part below."""
+    w = I.CAUSAL_8K_D64_WIDE
+    t = I.make_inputs(w)
+    say(w.name)
+    o, l = run_fwd(t, w.causal)
+    return w, t, o, l
+
+
+WIDE_PARTS = 8
+
+
+@pytest.mark.parametrize("part", range(WIDE_PARTS))
+def test_fwd_8k_d64_wide_scores_every_row(wide_scores_run, part):
+    """Every row of every head against the oracle, eight heads per part (the
+    oracle runs the heads of a part in parallel threads).  The relative L2
+    bound is checked per part, which implies it for the whole tensor."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    w, t, o, l = wide_scores_run
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    heads = heads[part * len(heads) // WIDE_PARTS:(part + 1) * len(heads) // WIDE_PARTS]
+
+    def ref(bh):
+        b, h = bh
+        return oracle.attention_forward(*(I.to_f64(t[n][b, h]) for n in ("q", "k", "v")), w.scale, w.causal)
+
+    with ThreadPoolExecutor(max_workers=min(len(heads), os.cpu_count() or 1)) as ex:
+        refs = list(ex.map(ref, heads))
+    og = np.stack([o[b, h] for b, h in heads])
+    lg = np.stack([l[b, h] for b, h in heads])
+    check_fwd(og, lg, np.stack([r[0] for r in refs]), np.stack([r[1] for r in refs]),
+              f"{w.name} heads {heads[0]}..{heads[-1]}")
+
+
+@pytest.mark.parametrize("w", [I.CAUSAL_32K_D128], ids=lambda w: w.name)
 def test_fwd_long_causal_sampled_rows(w):
-    """Full-size launch; the oracle evaluates 256 seeded rows of every head."""
+    """Full-size launch; the oracle evaluates 256 seeded rows of every head
+    (the seeded sample of the 32k workload)."""
     t = I.make_inputs(w)
     say(w.name)
     o, l = run_fwd(t, w.causal)
@@ -340,6 +379,58 @@ def test_fwd_scale_argument():
     o, l = run_fwd(t, True, scale=0.37)
     oref, lref = oracle_fwd(t, True, 0.37)
     check_fwd(o, l, oref, lref, "scale 0.37")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_scale_zero_weighs_visible_keys_equally(d):
+    """scale = 0: every visible key has weight 1/count (O = mean of the visible
+    V, L = ln(count)), and the gradients with respect to Q and K vanish."""
+    N = 333
+    t = shape_inputs(1, 2, N, d, "bf16", 304 + d, with_do=True)
+    for causal in (False, True):
+        o, l = run_fwd(t, causal, scale=0.0)
+        v = I.to_f64(t["v"])
+        if causal:
+            ref = np.cumsum(v, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+            lref = np.broadcast_to(np.log(np.arange(1, N + 1)), l.shape)
+        else:
+            ref = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+            lref = np.full(l.shape, math.log(N))
+        check_fwd(o, l, ref, lref, f"scale 0 d={d} causal={causal}", omax=1e-5, orel=1e-5, lmax=1e-5)
+        q, k, vv, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
+        og, lg = fa.forward(q, k, vv, causal=causal, scale=0.0)
+        dq, dk, dv = fa.backward(q, k, vv, og, lg, do, causal=causal, scale=0.0)
+        torch.cuda.synchronize()
+        gref = oracle_bwd(t, causal, 0.0)
+        assert float(dq.abs().max()) <= 1e-20 and float(dk.abs().max()) <= 1e-20
+        check_bwd((dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()), gref, f"scale 0 d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_negative_scale(d, causal):
+    """A negative scale reverses the order of the scores; forward and
+    backward against the oracle at the same scale."""
+    t = shape_inputs(1, 2, 300, d, "bf16", 305 + d, with_do=True)
+    sc = -1.3 / math.sqrt(d)
+    o, l = run_fwd(t, causal, scale=sc)
+    oref, lref = oracle_fwd(t, causal, sc)
+    check_fwd(o, l, oref, lref, f"scale {sc:.3f} d={d} causal={causal}")
+    q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
+    og, lg = fa.forward(q, k, v, causal=causal, scale=sc)
+    got = fa.backward(q, k, v, og, lg, do, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    check_bwd([x.cpu().numpy() for x in got], oracle_bwd(t, causal, sc), f"scale {sc:.3f} d={d} causal={causal}")
+    # the float32 kernel and the split-KV / few-row path at the same scale
+    t32 = shape_inputs(1, 2, 129, d, "f32", 306 + d)
+    o, l = run_fwd(t32, causal, scale=sc)
+    oref, lref = oracle_fwd(t32, causal, sc)
+    check_fwd(o, l, oref, lref, f"f32 scale {sc:.3f} d={d} causal={causal}", omax=1e-5, orel=1e-5, lmax=1e-5)
+    tg = I.make_general(1, 2, 2, 3000, d, d, 307 + d)
+    o, l = fa.forward_splitkv(*(tg[n].cuda() for n in ("q", "k", "v")), causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    oref, lref = oracle_fwd(tg, causal, sc)
+    check_fwd(o.cpu().numpy(), l.cpu().numpy(), oref, lref, f"split-KV scale {sc:.3f} d={d} causal={causal}")
 
 
 def test_empty_problem_is_a_noop():

@@ -1,7 +1,7 @@
 """GPU parity of packed variable-length attention (fa_fwd_varlen /
 fa_bwd_varlen) against the float64 per-sequence oracle (oracle/varlen.py).
 Sequences include lengths 0 and 1 and ragged tile tails; tolerances as in
-test_gpu_parity (O 1e-2 / 5e-3, gradients 2e-2 / 2e-2, L 1e-3)."""
+test_gpu_parity (O 1e-2 / 5e-3, gradients 1e-2 max-abs / 2e-2 relative L2, L 1e-3)."""
 
 import math
 import sys
@@ -16,7 +16,7 @@ from oracle import varlen as VL
 pytestmark = pytest.mark.gpu
 
 O_MAX, O_REL = 1e-2, 5e-3
-G_MAX, G_REL = 2e-2, 2e-2
+G_MAX, G_REL = 1e-2, 2e-2
 L_MAX = 1e-3
 
 
