@@ -76,6 +76,8 @@ def library():
         i64p = ctypes.POINTER(ctypes.c_int64)
         lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, f, i, vp]
         lib.fa_fwd_strided.restype = i
+        lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd_noalloc.restype = i
         lib.fa_dropout_applied_p.argtypes = [f]
         lib.fa_dropout_applied_p.restype = f
         lib.fa_status_string.argtypes = [i]

@@ -229,6 +229,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const fl
                                         N, d, scale, causal, nullptr, nullptr, stream));
 }
 
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                   float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+                   hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (2 * (unsigned long long)B * (unsigned long long)H * (unsigned long long)N > fa::scratch_floats())
+    return FA_ERR_SCRATCH;
+  float* ws = nullptr;
+  if (fa::scratch_on_current_device(&ws) != hipSuccess) return FA_ERR_HIP;
+  return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, ws, B * H, N, d, scale, causal, nullptr,
+                                        nullptr, stream));
+}
+
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
                    float* dq, float* dk, float* dv, void* workspace, int B, int H, int N, int d, float scale,
                    int causal, float p_drop, uint64_t seed, uint32_t offset, hipStream_t stream) {
@@ -323,6 +340,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "workspace is NULL";
     case FA_ERR_HIP: return "HIP runtime rejected a kernel launch";
     case FA_ERR_DROPOUT: return "dropout probability must be in [0, 1)";
+    case FA_ERR_SCRATCH: return "problem too large for the built-in scratch (B*H*N above 2^21 query rows)";
     default: return "unknown fa_status";
   }
 }

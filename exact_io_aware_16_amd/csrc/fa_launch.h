@@ -64,6 +64,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            float* dk, float* dv, int BH, int N, int d, float scale, int causal, const Dropout* drop,
                            const Seqs* seqs, hipStream_t stream);
 
+// The allocation-free backward's scratch (fa_scratch.hip): its capacity in
+// floats, and its device address on the current device (looked up once per
+// device).
+size_t scratch_floats();
+hipError_t scratch_on_current_device(float** out);
+
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* dvec, int BH, int N,
                            int d, float scale, int causal, const Dropout* drop, const Seqs* seqs,

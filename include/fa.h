@@ -56,7 +56,8 @@ typedef enum {
   FA_ERR_SCALE = 4,     /* scale is not finite (inf or NaN)                    */
   FA_ERR_WORKSPACE = 5, /* a required workspace is NULL                        */
   FA_ERR_HIP = 6,       /* a kernel launch was rejected by the HIP runtime     */
-  FA_ERR_DROPOUT = 7    /* dropout probability not in [0, 1)                   */
+  FA_ERR_DROPOUT = 7,   /* dropout probability not in [0, 1)                   */
+  FA_ERR_SCRATCH = 8    /* fa_bwd_noalloc: B*H*N above its scratch (2^21 rows) */
 } fa_status;
 
 /*
@@ -167,6 +168,27 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 int fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
            const void* dout, float* dq, float* dk, float* dv, void* workspace,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, layouts, results and
+ * errors as fa_bwd, minus `workspace`: the two float32 per query row that
+ * fa_bwd keeps in the caller's workspace live in a 16 MiB array inside the
+ * library instead, one copy per GPU, held until the process ends.  The call
+ * allocates and frees nothing.
+ *   Limit: B*H*N <= 2^21 query rows, otherwise FA_ERR_SCRATCH (nothing is
+ *   launched).  The array of the current device (hipGetDevice) is used:
+ *   `stream` must belong to that device.
+ *   Every call on one GPU shares that array and it keeps the last call's
+ *   contents (each call writes every row it reads first, so nothing needs
+ *   clearing): calls that overlap in time on one GPU -- on different streams,
+ *   or from several host threads -- race and give undefined results; order
+ *   them on one stream or synchronise between them.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                   const void* dout, float* dq, float* dk, float* dv,
+                   int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
  * Attention dropout whose mask the backward regenerates from the generator
