@@ -9,7 +9,16 @@ the step: 3.5 * (4*B*H*N^2*d / 2) FLOP per step (forward counted as
 4*B*H*N^2*d halved for causal, backward as 2.5x the forward).
 
 Also reported on the same line:
-  fwd        forward alone on B=1, H=8, N=4096, d=128, non-causal
+  configs    every measured workload (1: float32 tiny check, 2: forward
+             B1 H8 N4096 d128, 3: causal forward B4 H16 N8192 d64 with wide
+             scores, 4: causal forward B1 H8 N32768 d128, 5: the step), each
+             with its time, TFLOP/s, share of the bf16 peak, its roofline
+             (counter traffic when current) and the oracle timed on a
+             bounded sample of it (cpu_oracle)
+  n_doubling the forward workload at N = 4096 and N = 8192: per-head HBM bytes
+             from the committed counters (about 2x, not 4x: no N x N tensor
+             reaches HBM)
+  fwd        the forward workload (2) again, with its roofline
   decode     split-KV forward (fa_fwd_splitkv), one query row per head against
              32768 keys, B=1, H=32, d=dv=128, against the HBM roofline
   dropout    the step's forward and backward with dropout p = 0.1
@@ -23,7 +32,9 @@ Also reported on the same line:
   roofline   the dominant kernel of the step against the bf16 matrix-core
              peak; traffic from committed rocprofv3 counters when they were
              taken on the current kernel sources
-  cpu_baseline  the float64 oracle on a bounded sample of the workload
+  environment  ROCm version, gfx target, torch version, and the shader clock
+             sampled during the timed steps
+  cpu_baseline  the float64 oracle on a bounded sample of the step's workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -87,6 +98,116 @@ def steady(fn, seconds):
         torch.cuda.synchronize()
         if time.perf_counter() - t0 > seconds:
             break
+
+
+class ClockSampler:
+    """Samples the shader clock (MHz) from the driver's DPM table in sysfs
+    while it runs (the current level is the starred line of pp_dpm_sclk),
+    for the card whose PCI address is torch's device 0."""
+
+    def __init__(self, period_s=0.01):
+        import threading
+
+        self.path = self._sclk_path()
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _sclk_path():
+        import glob
+
+        try:
+            import torch
+
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+        except Exception:
+            bus = None
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        for c in cards:
+            try:
+                slot = [l for l in open(os.path.join(os.path.dirname(c), "uevent")) if l.startswith("PCI_SLOT_NAME=")]
+                if bus is not None and slot and int(slot[0].strip().split(":")[-2], 16) == bus:
+                    return c
+            except (OSError, ValueError):
+                continue
+        return cards[0] if len(cards) == 1 else None
+
+    def _read(self):
+        for line in open(self.path):
+            if line.rstrip().endswith("*"):
+                mhz = line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", "")
+                return float(mhz)
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None and v > 200:  # deep-sleep entries are not a running clock
+                    self.samples.append(v)
+            except (OSError, ValueError):
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"source": self.path or "no pp_dpm_sclk readable", "samples": 0}
+        xs = sorted(self.samples)
+        return {"source": self.path, "samples": len(xs), "min_mhz": xs[0], "median_mhz": xs[len(xs) // 2],
+                "max_mhz": xs[-1]}
+
+
+def environment(clock):
+    import torch
+
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        rocm = None
+    p = torch.cuda.get_device_properties(0)
+    return {"rocm": rocm, "gfx": p.gcnArchName, "device": p.name, "compute_units": p.multi_processor_count,
+            "torch": torch.__version__, "sclk_during_timed_steps": clock.summary()}
+
+
+def cpu_oracle_forward(w, t, rows_per_head=None, budget_s=5.0):
+    """The oracle's forward (untuned) on whole heads of a forward workload
+    until ~budget_s of work; rows_per_head limits each head to a seeded
+    sample of rows (the long workload).  GFLOP/s counts the sample's share
+    of the workload's forward FLOP."""
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from exact_io_aware_16_amd.inputs import sample_rows, to_f64
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = rows = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        r = None if rows_per_head is None else sample_rows(w.N, rows_per_head, 1000 * w.case + b * w.H + h)
+        oracle.attention_forward(*(to_f64(t[n][b, h]) for n in ("q", "k", "v")), w.scale, w.causal, rows=r)
+        done += 1
+        rows += w.N if r is None else len(r)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    # FLOP of the rows evaluated: the full-row FLOP per row scaled by the rows
+    flop = w.fwd_flop() * rows / (w.B * w.H * w.N)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    what = "full rows" if rows_per_head is None else f"{rows_per_head} seeded rows per head"
+    return {"seconds": round(el, 3), "gflops": round(flop / el / 1e9, 2), "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads, {what}, float64 forward"}
 
 
 def cpu_baseline(w, t, budget_s=12.0):
@@ -190,11 +311,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: exactly --steps steps, synchronised on both sides
-    t_start = time.perf_counter()
-    ms_step = time_calls(step, args.steps, stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+    # timed region: exactly --steps steps, synchronised on both sides; the
+    # shader clock is sampled meanwhile
+    with ClockSampler() as clock:
+        t_start = time.perf_counter()
+        ms_step = time_calls(step, args.steps, stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
     step_flop = 3.5 * w.fwd_flop()
     value = step_flop / (ms_step * 1e-3) / 1e12
 
@@ -223,6 +346,63 @@ def main():
     ms_f2 = time_calls(fwd2, args.steps, stream)
     f2 = wf.fwd_flop() / (ms_f2 * 1e-3) / 1e12
     f2_traffic, f2_src = committed_traffic("fwd_d128_split2")
+
+    # ------------------------------------------------------------ the other forward workloads
+    def time_forward(wl, seconds=0.5):
+        """Steady-state ms per forward call of workload wl (inputs resident)."""
+        tw = I.make_inputs(wl)
+        qw, kw, vw = (tw[n].to(dev) for n in ("q", "k", "v"))
+        ow = torch.empty((wl.B, wl.H, wl.N, wl.d), dtype=torch.float32, device=dev)
+        lw = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+
+        def call():
+            fa.forward(qw, kw, vw, causal=wl.causal, out=ow, lse=lw)
+
+        steady(call, seconds)
+        for _ in range(args.warmup):
+            call()
+        ms_w = time_calls(call, args.steps, stream)
+        del qw, kw, vw, ow, lw
+        return tw, ms_w
+
+    def roofline(flop, ms_w, entry, kernel):
+        tr, src = committed_traffic(entry)
+        ach = flop / (ms_w * 1e-3) / 1e12
+        return {"kernel": kernel, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": tr,
+                "traffic_source": src, "algorithmic_flop_per_launch": flop}
+
+    cfg = {}
+    t1, ms1 = time_forward(I.TINY_F32)
+    cfg["1"] = {"workload": I.TINY_F32.name, "ms": round(ms1, 4),
+                "tflops": round(I.TINY_F32.fwd_flop() / (ms1 * 1e-3) / 1e12, 3),
+                "bound": "latency (one workgroup per 64 rows; not a roofline case)", "dtype": "f32"}
+    cfg["2"] = {"workload": wf.name, "ms": round(ms_f2, 4), "tflops": round(f2, 2),
+                "pct_of_peak": round(100 * f2 / PEAK_BF16_TFLOPS, 2),
+                "roofline": roofline(wf.fwd_flop(), ms_f2, "fwd_4k",
+                                     "fwd_bf16_kernel<128, non-causal, split-KV x2> (the launch this grid gets)")}
+    for key, wl, entry, kname in (("3", I.CAUSAL_8K_D64_WIDE, "fwd_8k_d64_wide", "fwd_bf16_kernel<64, causal>"),
+                                  ("4", I.CAUSAL_32K_D128, "fwd_32k", "fwd_bf16_kernel<128, causal>")):
+        tw, ms_w = time_forward(wl)
+        tfw = wl.fwd_flop() / (ms_w * 1e-3) / 1e12
+        cfg[key] = {"workload": wl.name, "ms": round(ms_w, 4), "tflops": round(tfw, 2),
+                    "pct_of_peak": round(100 * tfw / PEAK_BF16_TFLOPS, 2),
+                    "roofline": roofline(wl.fwd_flop(), ms_w, entry, kname)}
+        cfg[key]["_inputs"] = tw
+    cfg["5"] = {"workload": w.name, "step_ms": round(ms_step, 4), "step_tflops": round(value, 2),
+                "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2), "fwd_ms": None, "bwd_ms": None}
+    # the N-doubling check: the forward workload at twice the rows
+    _, ms_8k = time_forward(I.FWD_8K_D128)
+    dbl = {"workloads": [wf.name, I.FWD_8K_D128.name], "ms": [round(ms_f2, 4), round(ms_8k, 4)]}
+    b4, src4 = committed_traffic("fwd_4k")
+    b8, _ = committed_traffic("fwd_8k")
+    if b4 is not None and b8 is not None:
+        heads = wf.B * wf.H
+        dbl.update({"hbm_bytes_per_head": [round(b4 / heads), round(b8 / heads)], "ratio": round(b8 / b4, 3),
+                    "materialised_score_bytes_per_head": [wf.N ** 2 * 4, I.FWD_8K_D128.N ** 2 * 4],
+                    "traffic_source": src4})
+    else:
+        dbl.update({"hbm_bytes_per_head": None, "ratio": None, "traffic_source": src4})
 
     # ------------------------------------------------------------ decode (split-KV across workgroups)
     dc = I.DECODE_32K
@@ -380,8 +560,24 @@ def main():
         },
         "timed_wall_s": round(wall, 3),
     }
+    cfg["5"]["fwd_ms"], cfg["5"]["bwd_ms"] = res["phases"]["fwd_ms"], res["phases"]["bwd_ms"]
+    cfg["5"]["fwd_tflops"], cfg["5"]["bwd_tflops"] = res["phases"]["fwd_tflops"], res["phases"]["bwd_tflops"]
+    cfg["5"]["roofline"] = res["roofline"]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, t)
+        cfg["1"]["cpu_oracle"] = cpu_oracle_forward(I.TINY_F32, t1, budget_s=1.0)
+        cfg["2"]["cpu_oracle"] = cpu_oracle_forward(wf, tf, budget_s=4.0)
+        cfg["3"]["cpu_oracle"] = cpu_oracle_forward(I.CAUSAL_8K_D64_WIDE, cfg["3"]["_inputs"], budget_s=4.0)
+        cfg["4"]["cpu_oracle"] = cpu_oracle_forward(I.CAUSAL_32K_D128, cfg["4"]["_inputs"], rows_per_head=256,
+                                                    budget_s=4.0)
+        cb = res["cpu_baseline"]
+        cfg["5"]["cpu_oracle"] = {"seconds": round(cb["seconds"], 3), "gflops": round(cb["value"] * 1e3, 2),
+                                  "cores": cb["cores"], "kind": "oracle", "sample": cb["sample"]}
+    for c in cfg.values():
+        c.pop("_inputs", None)
+    res["configs"] = cfg
+    res["n_doubling"] = dbl
+    res["environment"] = environment(clock)
     print(json.dumps(res), flush=True)
 
 

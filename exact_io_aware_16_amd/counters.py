@@ -81,6 +81,12 @@ def kernel_key(name):
     return None
 
 
+def _counted_workloads():
+    from exact_io_aware_16_amd import inputs as I
+
+    return (I.FWD_4K_D128, I.FWD_8K_D128, I.CAUSAL_8K_D64_WIDE, I.CAUSAL_32K_D128, I.FWDBWD_4K_D128)
+
+
 def run():
     import torch
 
@@ -88,18 +94,20 @@ def run():
     from exact_io_aware_16_amd import inputs as I
 
     dev = torch.device("cuda:0")
-    # the forward workload (its grid takes the split-KV launch) and the
-    # forward+backward workload (every kernel of the step)
-    for w in (I.FWD_4K_D128, I.FWDBWD_4K_D128):
+    # the forward workloads (4k, its 8k double, the wide-score d = 64 one, the
+    # 32k one) and the forward+backward workload (every kernel of the step)
+    for w in _counted_workloads():
         t = I.make_inputs(w)
         q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
-        for _ in range(REPEAT):
+        reps = REPEAT if w.N <= 8192 else 2
+        for _ in range(reps):
             o, lse = fa.forward(q, k, v, causal=w.causal)
         if w.backward:
             do = t["do"].to(dev)
             for _ in range(REPEAT):
                 fa.backward(q, k, v, o, lse, do, causal=w.causal)
         torch.cuda.synchronize()
+        del q, k, v, o, lse
         print(f"ran {w.name}", flush=True)
     # the decode workload: one query row per head against 32768 keys
     dc = I.DECODE_32K
@@ -128,6 +136,8 @@ def _read_counter_csv(d):
 
 
 def _per_kernel_mean(rows, counter):
+    """Mean counter value per launch, keyed "kernel@workgroups": one kernel
+    serves several workloads, and the workgroup count tells them apart."""
     acc = {}
     for r in rows:
         if r.get("Counter_Name") != counter:
@@ -135,6 +145,8 @@ def _per_kernel_mean(rows, counter):
         key = kernel_key(r.get("Kernel_Name", ""))
         if key is None:
             continue
+        if key != "copy":
+            key += "@" + str(int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
         acc.setdefault(key, []).append(float(r["Counter_Value"]))
     # the runtime's small host-to-device copies run the same copy kernel as
     # the calibration copy: calibrate on the large copy's dispatches only
@@ -177,13 +189,14 @@ def summarize(args):
     f_fetch = COPY_BYTES / (fetch["copy"] * 1024.0)
     f_write = COPY_BYTES / (write["copy"] * 1024.0)
     kernels = {}
-    for key in sorted(set(fetch) & set(write)):
-        if key == "copy":
+    for launch in sorted(set(fetch) & set(write)):
+        if launch not in BY_LAUNCH:
             continue
-        fb = fetch[key] * 1024.0 * f_fetch
-        wb = write[key] * 1024.0 * f_write
-        kernels[key] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes_per_launch": fb + wb,
-                        "fetch_kib_raw": fetch[key], "write_kib_raw": write[key]}
+        fb = fetch[launch] * 1024.0 * f_fetch
+        wb = write[launch] * 1024.0 * f_write
+        kernels[BY_LAUNCH[launch]] = {"launch": launch, "fetch_bytes": fb, "write_bytes": wb,
+                                      "hbm_bytes_per_launch": fb + wb, "fetch_kib_raw": fetch[launch],
+                                      "write_kib_raw": write[launch]}
     rec = {
         "source_sha256": kernel_source_digest(),
         "calibration": {"copy_bytes_each_way": COPY_BYTES, "fetch_kib_raw": fetch["copy"],
@@ -196,7 +209,8 @@ def summarize(args):
         names = sorted({r["Counter_Name"] for r in rows})
         for n in names:
             for k, v in _per_kernel_mean(rows, n).items():
-                sq.setdefault(k, {})[n] = v
+                if k in BY_LAUNCH:
+                    sq.setdefault(BY_LAUNCH[k], {})[n] = v
         rec["sq"] = sq
     if args.stats:
         rec["kernel_stats"] = _read_stats(args.stats)
@@ -205,78 +219,99 @@ def summarize(args):
     with open(os.path.join(args.out, "counters_attention_kernels.md"), "w") as f:
         f.write(markdown_counters(rec, args))
     if args.stats:
-        with open(os.path.join(args.out, "kernel_trace_bench_step_and_fwd.md"), "w") as f:
+        with open(os.path.join(args.out, "kernel_trace_bench_workloads.md"), "w") as f:
             f.write(markdown_stats(rec["kernel_stats"], args))
     print(json.dumps(rec, indent=1, sort_keys=True))
 
 
+def _fwd_bytes(BH, N, d):
+    """Q, K, V read once (bf16), O and L written once (float32)."""
+    return 3 * BH * N * d * 2 + BH * N * d * 4 + BH * N * 4
+
+
 _F5 = 2.0 * 32 * 4096 ** 2 * 128  # forward FLOP of B=2 H=16 N=4096 d=128 causal (two products)
-# workgroups of the launch each ALGORITHMIC entry describes: 128 query (or
-# key) rows per workgroup, 16 rows per workgroup for the prep kernel
-GRID = {"fwd_d128_split2": 8 * 32, "fwd_d128_causal": 32 * 32, "bwd_pre_d128": 32 * 4096 // 16,
-        "bwd_dkdv_d128_causal": 32 * 32, "bwd_dq_d128_causal": 32 * 32,
-        "decode_d128_rows1": 32 * 16, "splitkv_merge_dv128": 32}
-ALGORITHMIC = {
-    # key: (workload, algorithmic HBM bytes per launch, algorithmic FLOP per launch,
-    #       FLOP the kernel executes per launch)
-    "fwd_d128_split2": ("B=1 H=8 N=4096 d=128 non-causal",
-                        3 * 8 * 4096 * 128 * 2 + 8 * 4096 * 128 * 4 + 8 * 4096 * 4,
-                        4.0 * 8 * 4096 ** 2 * 128, 4.0 * 8 * 4096 ** 2 * 128),
-    "fwd_d128_causal": ("B=2 H=16 N=4096 d=128 causal", 3 * 32 * 4096 * 128 * 2 + 32 * 4096 * 128 * 4 + 32 * 4096 * 4,
-                        _F5, _F5),
+# Counted launches: entry -> (kernel key, workgroups of the launch, workload,
+# algorithmic HBM bytes per launch, algorithmic FLOP, FLOP the kernel executes).
+# Workgroups: 128 query (or key) rows per workgroup; the 4k forward's grid
+# (256 of them) takes the 8-wave launch with two key ranges per workgroup;
+# 16 rows per workgroup for the preprocess; 16 key ranges x 32 heads for decode.
+COUNTED = {
+    "fwd_4k": ("fwd_d128_split2", 8 * 32, "B=1 H=8 N=4096 d=128 non-causal",
+               _fwd_bytes(8, 4096, 128), 4.0 * 8 * 4096 ** 2 * 128, 4.0 * 8 * 4096 ** 2 * 128),
+    "fwd_8k": ("fwd_d128", 8 * 64, "B=1 H=8 N=8192 d=128 non-causal",
+               _fwd_bytes(8, 8192, 128), 4.0 * 8 * 8192 ** 2 * 128, 4.0 * 8 * 8192 ** 2 * 128),
+    "fwd_8k_d64_wide": ("fwd_d64_causal", 64 * 64, "B=4 H=16 N=8192 d=64 causal, qk std 3",
+                        _fwd_bytes(64, 8192, 64), 2.0 * 64 * 8192 ** 2 * 64, 2.0 * 64 * 8192 ** 2 * 64),
+    "fwd_32k": ("fwd_d128_causal", 8 * 256, "B=1 H=8 N=32768 d=128 causal",
+                _fwd_bytes(8, 32768, 128), 2.0 * 8 * 32768 ** 2 * 128, 2.0 * 8 * 32768 ** 2 * 128),
+    "fwd_step": ("fwd_d128_causal", 32 * 32, "B=2 H=16 N=4096 d=128 causal", _fwd_bytes(32, 4096, 128), _F5, _F5),
     # reads dO (bf16), O and L (float32); writes scale*D and L log2(e)
-    "bwd_pre_d128": ("B=2 H=16 N=4096 d=128", 32 * 4096 * 128 * (2 + 4) + 32 * 4096 * 4 * 3, 0.0, 0.0),
+    "bwd_prep": ("bwd_pre_d128", 32 * 4096 // 16, "B=2 H=16 N=4096 d=128",
+                 32 * 4096 * 128 * (2 + 4) + 32 * 4096 * 4 * 3, 0.0, 0.0),
     # reads Q, K, V, dO and the two workspace floats per row; writes dK, dV.
     # S, dP, dV, dK: four of the backward's five products
-    "bwd_dkdv_d128_causal": ("B=2 H=16 N=4096 d=128 causal",
-                             4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 2 * 32 * 4096 * 128 * 4, 2.0 * _F5, 2.0 * _F5),
+    "bwd_dkdv": ("bwd_dkdv_d128_causal", 32 * 32, "B=2 H=16 N=4096 d=128 causal",
+                 4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 2 * 32 * 4096 * 128 * 4, 2.0 * _F5, 2.0 * _F5),
     # reads Q, K, V, dO and the workspace; writes dQ.  dQ is the fifth product;
     # S and dP are computed a second time (1.5x the forward executed)
-    "bwd_dq_d128_causal": ("B=2 H=16 N=4096 d=128 causal",
-                           4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 32 * 4096 * 128 * 4, 0.5 * _F5, 1.5 * _F5),
+    "bwd_dq": ("bwd_dq_d128_causal", 32 * 32, "B=2 H=16 N=4096 d=128 causal",
+               4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 32 * 4096 * 128 * 4, 0.5 * _F5, 1.5 * _F5),
     # decode, 16 key ranges: reads Q, K, V once, writes 16 partial (O, L) per row
-    "decode_d128_rows1": ("decode B=1 H=32 Nq=1 Nk=32768 d=128",
-                          32 * 128 * 2 + 2 * 32 * 32768 * 128 * 2 + 16 * 32 * 129 * 4, 0.0, 0.0),
+    "decode": ("decode_d128_rows1", 32 * 16, "decode B=1 H=32 Nq=1 Nk=32768 d=128",
+               32 * 128 * 2 + 2 * 32 * 32768 * 128 * 2 + 16 * 32 * 129 * 4, 0.0, 0.0),
     # reads the 16 partials per row, writes O and L
-    "splitkv_merge_dv128": ("decode B=1 H=32 Nq=1 Nk=32768 d=128", 16 * 32 * 129 * 4 + 32 * 129 * 4, 0.0, 0.0),
+    "decode_merge": ("splitkv_merge_dv128", 32, "decode B=1 H=32 Nq=1 Nk=32768 d=128",
+                     16 * 32 * 129 * 4 + 32 * 129 * 4, 0.0, 0.0),
 }
+# the same table by "kernel@workgroups" (the key of the counter records)
+BY_LAUNCH = {f"{v[0]}@{v[1]}": k for k, v in COUNTED.items()}
 
 
 def markdown_counters(rec, args):
     cal = rec["calibration"]
     out = ["# Hardware counters of the attention kernels (MI355X)", "",
-           "Collected with the committed driver `exact_io_aware_16_amd/counters.py` (5 launches of each",
-           "kernel on the forward workload B=1,H=8,N=4096,d=128 and the forward+backward workload",
-           "B=2,H=16,N=4096,d=128 causal, the decode call B=1,H=32, one query row, 32768 keys, d=128,",
-           "plus a 512 MiB device copy for calibration), one counter group",
-           "per run:", "", "```",
+           "Collected with the committed driver `exact_io_aware_16_amd/counters.py`: a few launches of",
+           "each kernel on every measured workload (the forward workloads at N = 4096 and its N = 8192",
+           "double, d = 64 wide scores at N = 8192, N = 32768 causal; the forward+backward workload",
+           "B=2,H=16,N=4096,d=128 causal; the decode call B=1,H=32, one query row, 32768 keys, d=128),",
+           "plus a 512 MiB device copy for calibration, one counter group per run:", "", "```",
            "cd /tmp && export TMPDIR=/tmp PYTHONPATH=$REPO",
            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o run -- python -u -m exact_io_aware_16_amd.counters run",
            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o run -- python -u -m exact_io_aware_16_amd.counters run",
            f"rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d $OUT/pmc_sq -o run -- python -u -m exact_io_aware_16_amd.counters run",
            "python -m exact_io_aware_16_amd.counters summarize --fetch $OUT/pmc_fetch --write $OUT/pmc_write --sq $OUT/pmc_sq --stats $OUT/prof_stats",
            "```", "",
-           f"Kernel-source digest: `{rec['source_sha256'][:16]}`.", "",
+           f"Kernel-source digest: `{rec['source_sha256'][:16]}`.  Launches are told apart by kernel and",
+           "workgroup count (one kernel serves several workloads).", "",
            "## HBM traffic per launch", "",
            f"Calibration: the 512 MiB copy reads FETCH_SIZE = {cal['fetch_kib_raw']:.0f} KiB and WRITE_SIZE = "
            f"{cal['write_kib_raw']:.0f} KiB, so the factors are {cal['fetch_factor']:.3f} (fetch) and "
            f"{cal['write_factor']:.3f} (write).", "",
-           "| kernel | workload | fetch MiB | write MiB | HBM MiB | algorithmic MiB | ratio |",
-           "|---|---|---|---|---|---|---|"]
-    for k, v in sorted(rec["kernels"].items()):
-        wl, alg, _, _ = ALGORITHMIC.get(k, ("", 0, 0, 0))
-        ratio = f"{v['hbm_bytes_per_launch'] / alg:.2f}" if alg else ""
-        out.append(f"| {k} | {wl} | {v['fetch_bytes'] / 2**20:.1f} | {v['write_bytes'] / 2**20:.1f} | "
-                   f"{v['hbm_bytes_per_launch'] / 2**20:.1f} | {alg / 2**20:.1f} | {ratio} |")
+           "| entry | kernel@workgroups | workload | fetch MiB | write MiB | HBM MiB | algorithmic MiB | ratio |",
+           "|---|---|---|---|---|---|---|---|"]
+    for k in COUNTED:
+        v = rec["kernels"].get(k)
+        if v is None:
+            continue
+        _, _, wl, alg, _, _ = COUNTED[k]
+        out.append(f"| {k} | {v['launch']} | {wl} | {v['fetch_bytes'] / 2**20:.1f} | {v['write_bytes'] / 2**20:.1f} | "
+                   f"{v['hbm_bytes_per_launch'] / 2**20:.1f} | {alg / 2**20:.1f} | "
+                   f"{v['hbm_bytes_per_launch'] / alg:.2f} |")
+    k4, k8 = rec["kernels"].get("fwd_4k"), rec["kernels"].get("fwd_8k")
+    if k4 and k8:
+        out += ["", f"N-doubling (8 heads both): {k4['hbm_bytes_per_launch'] / 8 / 2**20:.2f} MiB per head at N = 4096, "
+                f"{k8['hbm_bytes_per_launch'] / 8 / 2**20:.2f} MiB per head at N = 8192: "
+                f"{k8['hbm_bytes_per_launch'] / k4['hbm_bytes_per_launch']:.2f}x for twice the rows (4x would mean "
+                "an N x N term reaches HBM)."]
     if rec.get("sq"):
         out += ["", "## SQ counters per launch (raw sums over the device)", ""]
         names = sorted({n for d in rec["sq"].values() for n in d})
-        out.append("| kernel | " + " | ".join(names) + " |")
+        out.append("| entry | " + " | ".join(names) + " |")
         out.append("|---|" + "---|" * len(names))
-        for k, d in sorted(rec["sq"].items()):
-            if k == "copy":
-                continue
-            out.append(f"| {k} | " + " | ".join(f"{d.get(n, 0):.0f}" for n in names) + " |")
+        for k in COUNTED:
+            d = rec["sq"].get(k)
+            if d:
+                out.append(f"| {k} | " + " | ".join(f"{d.get(n, 0):.0f}" for n in names) + " |")
         out += ["", "SQ_VALU_MFMA_BUSY_CYCLES counts 32 per 32x32x16 bf16 MFMA summed over all SIMDs;",
                 "SQ_VALU_MFMA_COEXEC_CYCLES counts cycles where a vector instruction issued while the matrix",
                 "core was busy; SQ_WAIT_ANY / SQ_WAVE_CYCLES (both in quad-cycles) is the share of wave time",
@@ -293,28 +328,26 @@ def markdown_stats(stats, args):
            "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_stats -o run -- "
            "python -u $REPO/bench.py --no-cpu-baseline --steps 20 --warmup 5",
            "```", "",
-           "The bench first runs the fwd+bwd step (B=2,H=16,N=4096,d=128 causal) untimed for about a",
-           "second, then each of its kernels alone on the same inputs, then the timed steps, then the",
-           "forward workload B=1,H=8,N=4096,d=128, the decode workload (B=1, H=32, one query row, 32768",
-           "keys, d=128: decode_d128_rows1 on key ranges across workgroups, then splitkv_merge_dv128), and the",
-           "dropout (p = 0.1) and packed-sequence steps, the latter beside the same batch padded to",
-           "B=8.  Each workload runs about half a second untimed before it is timed.  One kernel serves",
-           "several of these workloads, so launches are grouped by kernel and workgroup count, taken",
-           "from the per-dispatch trace.  Algorithmic TFLOP/s counts the attention products the method",
-           "needs (forward 2, backward 5); executed TFLOP/s counts what the kernel runs (the dQ kernel",
-           "recomputes S and dP).  Both are given for the launch of the workload named beside them.",
-           "Rows without a workload: 4096 workgroups are the packed batch and its padded copy (8",
-           "sequences x 16 heads x 32 blocks each), decode_d128_rows1 and splitkv_merge_dv128 the decode",
-           "call, the _dropout keys the step with dropout, the other prep grids those of the packed and",
-           "padded batches.", "",
+           "The bench runs the fwd+bwd step (B=2,H=16,N=4096,d=128 causal) untimed for about a second,",
+           "then each of its kernels alone on the same inputs, then the timed steps, then the forward",
+           "workloads (B=1,H=8,N=4096,d=128; the float32 tiny check; B=4,H=16,N=8192,d=64 causal;",
+           "B=1,H=8,N=32768,d=128 causal; B=1,H=8,N=8192,d=128), the decode workload (B=1, H=32, one",
+           "query row, 32768 keys, d=128: decode_d128_rows1 on key ranges across workgroups, then",
+           "splitkv_merge_dv128), and the dropout (p = 0.1) and packed-sequence steps, the latter beside",
+           "the same batch padded to B=8.  Each workload runs about half a second untimed before it is",
+           "timed.  One kernel serves several of these workloads, so launches are grouped by kernel and",
+           "workgroup count, taken from the per-dispatch trace.  Algorithmic TFLOP/s counts the",
+           "attention products the method needs (forward 2, backward 5); executed TFLOP/s counts what",
+           "the kernel runs (the dQ kernel recomputes S and dP).  Both are given for the launch of the",
+           "workload named beside them; rows without a workload are the packed batch, its padded copy,",
+           "the dropout step and the float32 kernel.", "",
            "| kernel | workgroups | workload | calls | average us | min us | max us | algorithmic TFLOP/s | "
            "executed TFLOP/s |",
            "|---|---|---|---|---|---|---|---|---|"]
-    for _, v in sorted(stats.items(), key=lambda kv: (kv[1]["key"], kv[1]["workgroups"])):
+    for launch, v in sorted(stats.items(), key=lambda kv: (kv[1]["key"], kv[1]["workgroups"])):
         k = v["key"]
-        wl, _, flop, xflop = ALGORITHMIC.get(k, ("", 0, 0, 0))
-        if GRID.get(k) != v["workgroups"]:
-            wl, flop, xflop = "", 0, 0
+        entry = BY_LAUNCH.get(launch)
+        _, _, wl, _, flop, xflop = COUNTED[entry] if entry else ("", 0, "", 0, 0, 0)
         tf = f"{flop / (v['avg_ns'] * 1e-9) / 1e12:.1f}" if flop else ""
         xtf = f"{xflop / (v['avg_ns'] * 1e-9) / 1e12:.1f}" if xflop else ""
         out.append(f"| {k} | {v['workgroups']} | {wl} | {v['calls']} | {v['avg_ns'] / 1e3:.1f} | "

@@ -56,6 +56,10 @@ CAUSAL_8K_D64_WIDE = Workload("fwd_bf16_causal_b4h16n8192d64_qk3", 3, 4, 16, 819
                               note="forward, causal, Q and K ~ N(0, 3^2): the running max moves often")
 CAUSAL_32K_D128 = Workload("fwd_bf16_causal_b1h8n32768d128", 4, 1, 8, 32768, 128, True, "bf16",
                            sample_rows=256, note="long-context causal forward")
+# the forward workload at twice the sequence length: per-head HBM bytes of
+# the two should differ by about 2x (K and V re-reads absorbed on chip), not 4x
+FWD_8K_D128 = Workload("fwd_bf16_b1h8n8192d128", 2, 1, 8, 8192, 128, False, "bf16",
+                       note="forward, non-causal, twice the sequence length of the forward workload")
 FWDBWD_4K_D128 = Workload("fwdbwd_bf16_causal_b2h16n4096d128", 5, 2, 16, 4096, 128, True, "bf16",
                           backward=True, note="forward + recompute backward, causal")
 
