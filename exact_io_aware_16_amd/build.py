@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_decode.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_scratch.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_r64.hip", "fa_decode.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_scratch.hip"]
 ARCH = os.environ.get("FA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -682,6 +682,8 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o
   const Strides lay = strides ? *strides
                               : Strides{0, (long long)Nq * d, 0, (long long)Nk * d, 0, (long long)Nk * dv, d, d, dv, BH};
   const bool dense = strides == nullptr;
+  if (!drop && n_ksplit == 1 && fwd_r64_applies(d, dv))
+    return launch_fwd_r64(q, k, v, o, lse, BH, Nq, Nk, causal, scale, sq.cu ? &sq : nullptr, lay, stream);
   if (d == 128)
     return causal ? launch_dv<128, true>(q, k, v, o, lse, BH, Nq, Nk, dv, n_ksplit, ws, scale, drop, sq, lay, dense,
                                          stream)

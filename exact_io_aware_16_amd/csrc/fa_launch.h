@@ -32,6 +32,12 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, float* o
                            int Nk, int d, int dv, int causal, int n_ksplit, float* ws, float scale,
                            const Dropout* drop, const Seqs* seqs, hipStream_t stream,
                            const Strides* strides = nullptr);
+// Forward for d = dv = 128 without dropout or split-KV ranges
+// (fa_fwd_r64.hip), same arguments and layout as launch_fwd_bf16 with
+// n_ksplit = 1; launch_fwd_bf16 routes these calls here.
+bool fwd_r64_applies(int d, int dv);
+hipError_t launch_fwd_r64(const void* q, const void* k, const void* v, float* o, float* lse, int BH, int Nq, int Nk,
+                          int causal, float scale, const Seqs* seqs, const Strides& lay, hipStream_t stream);
 // Number of key ranges a split-KV forward uses for n_splits requested
 // (0: chosen for the grid); 1 means no split and no workspace.
 int fwd_splitkv_resolve(int BH, int Nq, int Nk, int d, int dv, int n_splits);

@@ -360,6 +360,50 @@ def test_fwd_late_max_rescale():
     check_fwd(o, l, oref, lref, "late max")
 
 
+def _rising_scores(B, H, N, gap_log2, seed, v_scale=1.0):
+    """Head width 128: every query is all ones and key j is t_j (1, ..., 1)
+    plus noise, with t_j rising along the keys so that the last key's score
+    is about gap_log2 (base-2 units of the scaled score) above the first's.
+    Each row's weights then grow along the keys, far past any reference taken
+    from the first keys."""
+    d = 128
+    t = shape_inputs(B, H, N, d, "bf16", seed)
+    g = torch.Generator().manual_seed(seed)
+    c = (1 / math.sqrt(d)) * math.log2(math.e)
+    top = gap_log2 / (c * d)
+    ramp = torch.linspace(0.0, top, N)[None, None, :, None]
+    t["q"] = torch.ones(B, H, N, d).to(torch.bfloat16)
+    t["k"] = (ramp + 0.05 * torch.randn(B, H, N, d, generator=g)).to(torch.bfloat16)
+    t["v"] = (v_scale * torch.randn(B, H, N, d, generator=g)).to(torch.bfloat16)
+    return t
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(1, 2, 2048), (1, 64, 1024)])
+@pytest.mark.parametrize("gap", [60.0, 110.0, 400.0])
+def test_fwd_d128_scores_rising_along_keys(B, H, N, gap, causal):
+    """Weights far above 1 relative to a row's first keys: gaps that stay
+    finite in float32 and one that overflows it.  Both must match the
+    oracle."""
+    t = _rising_scores(B, H, N, gap, 310)
+    o, l = run_fwd(t, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(128))
+    check_fwd(o, l, oref, lref, f"rising gap={gap} B={B} H={H} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_d128_large_values_with_rising_scores(causal):
+    """Values near 2^40 with weights up to about 2^100 relative to the first
+    keys: the weighted sum of values leaves float32 range unless the
+    reference is the true row max.  The result is the oracle's."""
+    B, H, N = 1, 4, 1536
+    vs = 2.0 ** 40
+    t = _rising_scores(B, H, N, 100.0, 311, v_scale=vs)
+    o, l = run_fwd(t, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(128))
+    check_fwd(o / vs, l, oref / vs, lref, f"large values causal={causal}")
+
+
 def test_fwd_kv_permutation_invariance():
     N, d = 333, 128
     t = shape_inputs(1, 2, N, d, "bf16", 302)
