@@ -293,12 +293,12 @@ def main():
     F = w.fwd_flop()
     kernels = {
         # name: (call, counter key, algorithmic FLOP, executed FLOP)
-        "fa_fwd": (fwd, "fwd_d128_causal", F, F),
-        "fa_bwd_prep": (lambda: fa.backward_prep(o, lse, do, ws), "bwd_pre_d128", 0.0, 0.0),
+        "fa_fwd": (fwd, "fwd_step", F, F),
+        "fa_bwd_prep": (lambda: fa.backward_prep(o, lse, do, ws), "bwd_prep", 0.0, 0.0),
         "fa_bwd_dkdv": (lambda: fa.backward_dkdv(q, k, v, do, ws, causal=True, dk=dk_o, dv=dv_o),
-                        "bwd_dkdv_d128_causal", 2.0 * F, 2.0 * F),
+                        "bwd_dkdv", 2.0 * F, 2.0 * F),
         "fa_bwd_dq": (lambda: fa.backward_dq(q, k, v, do, ws, causal=True, dq=dq_o),
-                      "bwd_dq_d128_causal", 0.5 * F, 1.5 * F),
+                      "bwd_dq", 0.5 * F, 1.5 * F),
     }
     kern = {}
     for name, (fn, key, flop, xflop) in kernels.items():
@@ -345,7 +345,7 @@ def main():
         fwd2()
     ms_f2 = time_calls(fwd2, args.steps, stream)
     f2 = wf.fwd_flop() / (ms_f2 * 1e-3) / 1e12
-    f2_traffic, f2_src = committed_traffic("fwd_d128_split2")
+    f2_traffic, f2_src = committed_traffic("fwd_4k")
 
     # ------------------------------------------------------------ the other forward workloads
     def time_forward(wl, seconds=0.5):
@@ -380,9 +380,9 @@ def main():
     cfg["2"] = {"workload": wf.name, "ms": round(ms_f2, 4), "tflops": round(f2, 2),
                 "pct_of_peak": round(100 * f2 / PEAK_BF16_TFLOPS, 2),
                 "roofline": roofline(wf.fwd_flop(), ms_f2, "fwd_4k",
-                                     "fwd_bf16_kernel<128, non-causal, split-KV x2> (the launch this grid gets)")}
+                                     "fwd_r64_kernel<non-causal, two key ranges per workgroup> (the launch this grid gets)")}
     for key, wl, entry, kname in (("3", I.CAUSAL_8K_D64_WIDE, "fwd_8k_d64_wide", "fwd_bf16_kernel<64, causal>"),
-                                  ("4", I.CAUSAL_32K_D128, "fwd_32k", "fwd_bf16_kernel<128, causal>")):
+                                  ("4", I.CAUSAL_32K_D128, "fwd_32k", "fwd_r64_kernel<causal>")):
         tw, ms_w = time_forward(wl)
         tfw = wl.fwd_flop() / (ms_w * 1e-3) / 1e12
         cfg[key] = {"workload": wl.name, "ms": round(ms_w, 4), "tflops": round(tfw, 2),
@@ -516,7 +516,7 @@ def main():
             "ms": round(ms_f2, 4),
             "tflops": round(f2, 2),
             "roofline": {
-                "kernel": "fwd_bf16_kernel<128, non-causal, split-KV x2> (the launch this grid gets)",
+                "kernel": "fwd_r64_kernel<non-causal, two key ranges per workgroup> (the launch this grid gets)",
                 "bound": "mfma",
                 "achieved": round(f2, 2),
                 "peak": PEAK_BF16_TFLOPS,

@@ -58,6 +58,9 @@ def kernel_key(name):
         drop = m.group(5) in ("1", "true")
         return (f"fwd_d{d}" + (f"_dv{dv}" if dv != d else "") + ("_causal" if causal else "")
                 + ("_split2" if split == "2" else "") + ("_dropout" if drop else ""))
+    m = re.search(r"fwd_r64_kernel(?:ILb|<)" + b + r"(?:ELi|, )(\d)", name)
+    if m:
+        return "fwd_r64" + ("_causal" if m.group(1) in ("1", "true") else "") + ("_split2" if m.group(2) == "2" else "")
     m = re.search(r"decode_kernel(?:ILi|<)(\d+)(?:ELi|, )(\d)(?:ELb|, )" + b, name)
     if m:
         return f"decode_d{m.group(1)}_rows{m.group(2)}" + ("_causal" if m.group(3) in ("1", "true") else "")
@@ -236,15 +239,15 @@ _F5 = 2.0 * 32 * 4096 ** 2 * 128  # forward FLOP of B=2 H=16 N=4096 d=128 causal
 # (256 of them) takes the 8-wave launch with two key ranges per workgroup;
 # 16 rows per workgroup for the preprocess; 16 key ranges x 32 heads for decode.
 COUNTED = {
-    "fwd_4k": ("fwd_d128_split2", 8 * 32, "B=1 H=8 N=4096 d=128 non-causal",
+    "fwd_4k": ("fwd_r64_split2", 8 * 32, "B=1 H=8 N=4096 d=128 non-causal",
                _fwd_bytes(8, 4096, 128), 4.0 * 8 * 4096 ** 2 * 128, 4.0 * 8 * 4096 ** 2 * 128),
-    "fwd_8k": ("fwd_d128", 8 * 64, "B=1 H=8 N=8192 d=128 non-causal",
+    "fwd_8k": ("fwd_r64", 8 * 32, "B=1 H=8 N=8192 d=128 non-causal",
                _fwd_bytes(8, 8192, 128), 4.0 * 8 * 8192 ** 2 * 128, 4.0 * 8 * 8192 ** 2 * 128),
     "fwd_8k_d64_wide": ("fwd_d64_causal", 64 * 64, "B=4 H=16 N=8192 d=64 causal, qk std 3",
                         _fwd_bytes(64, 8192, 64), 2.0 * 64 * 8192 ** 2 * 64, 2.0 * 64 * 8192 ** 2 * 64),
-    "fwd_32k": ("fwd_d128_causal", 8 * 256, "B=1 H=8 N=32768 d=128 causal",
+    "fwd_32k": ("fwd_r64_causal", 8 * 128, "B=1 H=8 N=32768 d=128 causal",
                 _fwd_bytes(8, 32768, 128), 2.0 * 8 * 32768 ** 2 * 128, 2.0 * 8 * 32768 ** 2 * 128),
-    "fwd_step": ("fwd_d128_causal", 32 * 32, "B=2 H=16 N=4096 d=128 causal", _fwd_bytes(32, 4096, 128), _F5, _F5),
+    "fwd_step": ("fwd_r64_causal", 32 * 16, "B=2 H=16 N=4096 d=128 causal", _fwd_bytes(32, 4096, 128), _F5, _F5),
     # reads dO (bf16), O and L (float32); writes scale*D and L log2(e)
     "bwd_prep": ("bwd_pre_d128", 32 * 4096 // 16, "B=2 H=16 N=4096 d=128",
                  32 * 4096 * 128 * (2 + 4) + 32 * 4096 * 4 * 3, 0.0, 0.0),
