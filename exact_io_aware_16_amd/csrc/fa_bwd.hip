@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   int bh, kvb;
   if (CAUSAL || seqs.cu) {
     if ((int)blockIdx.x >= total) return;
-    longest_first(blockIdx.x, total / n_kvblk, kvb, bh);  // key block 0 sees every query row
+    causal_order(blockIdx.x, total / n_kvblk, n_kvblk, kAllHeads, kvb, bh);  // key block 0 sees every query row
   } else {
     const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     if (blk >= total) return;

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   int bh, qblk;
   if (CAUSAL || seqs.cu) {
     if ((int)blockIdx.x >= total) return;
-    longest_first(blockIdx.x, total / n_qblk, qblk, bh);
+    causal_order(blockIdx.x, total / n_qblk, n_qblk, kAllHeads, qblk, bh);
     if (CAUSAL) qblk = n_qblk - 1 - qblk;  // the last query block sees every key
   } else {
     const int blk = xcd_logical_block(blockIdx.x, gridDim.x);

@@ -153,15 +153,38 @@ __device__ __forceinline__ void seq_range(const Seqs& sq, int b, int& s0, int& s
 }
 
 // Causal work items come in ranks of different length (the key range of a
-// query block, the query range of a key block), one item per head and rank.
-// Taking ids rank-major with the longest rank first -- id = rank * BH + head
-// -- and letting the hardware deal consecutive ids to the eight XCDs in turn
-// gives every XCD the same mix of lengths, queued longest first, which keeps
-// the tail of the launch short; when BH is a multiple of 8 all items of one
-// head still run on one XCD.  ids from BH * ranks on do nothing.
-__device__ __forceinline__ void longest_first(int bid, int BH, int& rank, int& head) {
-  rank = bid / BH;
-  head = bid - rank * BH;
+// query block, the query range of a key block), one item per head and rank,
+// rank 0 the longest.  The hardware deals consecutive ids to the eight XCDs
+// in turn, so XCD x runs ids x, x + 8, x + 16, ... in that order, each on
+// the next free CU.  With BH a multiple of 8, heads h = x (mod 8) go to XCD
+// x, which takes them in groups of G heads, rank-major inside a group
+// (longest first).  The items running at once on an XCD then stream the
+// K/V (or Q/dO) of at most G heads, which its L2 holds, and the lengths
+// still pair up long with short.  Otherwise ids are taken rank-major over
+// all heads, id = rank * BH + head, which is also what G >= BH / 8 gives.
+// ids from BH * n_rank on do nothing.
+//
+// Measured on MI355X (B=2, H=16, N=4096): one or two heads per group brings
+// the backward kernels' HBM bytes down to the algorithmic count, but costs
+// 1-3% of their time against rank-major order over all heads -- their
+// re-reads hit the L2 and the memory-side cache and never limit them -- so
+// the d = 128 kernels pass kAllHeads.  The 128-row forward kernel, which
+// runs two workgroups per CU over many heads, keeps two heads per group:
+// same time, a third of the HBM bytes.
+constexpr int kAllHeads = 1 << 30;
+__device__ __forceinline__ void causal_order(int bid, int BH, int n_rank, int G, int& rank, int& head) {
+  if ((BH & 7) == 0) {
+    const int x = bid & 7, s = bid >> 3;
+    const int hx = BH >> 3;  // heads per XCD
+    const int gs = min(G, hx);
+    const int gi = s / (gs * n_rank), w = s - gi * gs * n_rank;
+    const int in_group = min(gs, hx - gi * gs);  // the last group may be smaller
+    rank = w / in_group;
+    head = x + 8 * (gi * gs + (w - rank * in_group));
+  } else {
+    rank = bid / BH;
+    head = bid - rank * BH;
+  }
 }
 
 }  // namespace fa

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   int bh, rem;
   if (CAUSAL || seqs.cu) {
     if ((int)blockIdx.x >= total) return;
-    longest_first(blockIdx.x, total / per_head, rem, bh);
+    causal_order(blockIdx.x, total / per_head, per_head, 2, rem, bh);
   } else {
     const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
     if (blk >= total) return;

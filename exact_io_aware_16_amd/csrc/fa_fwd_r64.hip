@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_r64_kernel(
   int bh, qb;
   if (CAUSAL || seqs.cu) {
     if ((int)blockIdx.x >= total) return;
-    longest_first(blockIdx.x, total / n_qblk, qb, bh);
+    causal_order(blockIdx.x, total / n_qblk, n_qblk, kAllHeads, qb, bh);
     if (CAUSAL) qb = n_qblk - 1 - qb;  // longest rows first
   } else {
     const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
