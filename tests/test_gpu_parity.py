@@ -404,6 +404,37 @@ def test_fwd_d128_large_values_with_rising_scores(causal):
     check_fwd(o / vs, l, oref / vs, lref, f"large values causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_d128_rising_scores_general_and_strided(causal):
+    """The restart of a rising-score row through the other forward entry
+    points: Tq != Tk (fa_fwd_ex) and strided views of a packed projection
+    (fa_fwd_strided).  Both match the oracle."""
+    d, c = 128, (1 / math.sqrt(128)) * math.log2(math.e)
+    g = torch.Generator("cpu").manual_seed(312)
+    nq, nk = 300, 2000
+    ramp = torch.linspace(0.0, 400.0 / (c * d), nk)[None, None, :, None]
+    t = {"q": torch.ones(1, 2, nq, d).to(torch.bfloat16),
+         "k": (ramp + 0.05 * torch.randn(1, 2, nk, d, generator=g)).to(torch.bfloat16),
+         "v": torch.randn(1, 2, nk, d, generator=g).to(torch.bfloat16)}
+    o, l = run_fwd(t, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(d))
+    check_fwd(o, l, oref, lref, f"rising general Nq={nq} Nk={nk} causal={causal}")
+    # strided: Q, K, V as views of one [B, N, 3, H, d] tensor
+    B, H, N = 1, 2, 1500
+    qkv = torch.empty((B, N, 3, H, d))
+    qkv[:, :, 0] = 1.0
+    qkv[:, :, 1] = torch.linspace(0.0, 400.0 / (c * d), N)[None, :, None, None] + 0.05 * torch.randn(
+        (B, N, H, d), generator=g)
+    qkv[:, :, 2] = torch.randn((B, N, H, d), generator=g)
+    qkv = qkv.to(torch.bfloat16)
+    gqkv = qkv.cuda()
+    o_s, l_s = fa.forward(*[gqkv[:, :, j].permute(0, 2, 1, 3) for j in range(3)], causal=causal)
+    torch.cuda.synchronize()
+    views = [qkv[:, :, j].permute(0, 2, 1, 3).contiguous().to(torch.float64).numpy() for j in range(3)]
+    oref, lref = oracle.attention_forward_bhnd(*views, 1 / math.sqrt(d), causal)
+    check_fwd(o_s.cpu().numpy(), l_s.cpu().numpy(), oref, lref, f"rising strided causal={causal}")
+
+
 def test_fwd_kv_permutation_invariance():
     N, d = 333, 128
     t = shape_inputs(1, 2, N, d, "bf16", 302)

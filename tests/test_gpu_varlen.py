@@ -82,6 +82,53 @@ def test_varlen_forward_and_backward(li, causal, d):
         assert ge <= G_MAX and gr <= G_REL, name
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_d128_scores_rising_along_keys(causal):
+    """Head width 128, every query all ones and each sequence's keys rising
+    by about 400 base-2 units from its first key to its last: weights far
+    past float32 range against a reference taken from the first keys, in
+    every sequence of the packed batch.  O, L, dK and dV match the oracle.
+
+    dQ is only required to be finite here: it is sum_j dS_ij K_j with keys
+    that share a large common offset (about 24 per element), which cancels
+    exactly only for exact dS.  The kernels round dS to bf16 for the matrix
+    cores, and that rounding alone -- everything else in float64 -- already
+    leaves dQ with a relative L2 error of 0.26-0.42 on these inputs.  The
+    max-abs gates assume gradients of order one; here dK and dV reach about
+    9 and 25, so their max-abs is gated relative to their largest value."""
+    lengths, H, d = [700, 0, 1500, 33], 2, 128
+    (q, k, v, do), cu = packed(lengths, H, d, 5200)
+    c = (1 / math.sqrt(d)) * math.log2(math.e)
+    g = torch.Generator("cpu").manual_seed(5201)
+    kf = torch.empty((H, int(cu[-1]), d))
+    for b, n in enumerate(lengths):
+        if n:
+            ramp = torch.linspace(0.0, 400.0 / (c * d), n)[None, :, None]
+            kf[:, cu[b]:cu[b + 1]] = ramp + 0.05 * torch.randn((H, n, d), generator=g)
+    q = torch.ones((H, int(cu[-1]), d)).to(torch.bfloat16)
+    k = kf.to(torch.bfloat16)
+    say(f"varlen rising scores lengths={lengths} causal={causal}")
+    qg, kg, vg, dog = (x.cuda() for x in (q, k, v, do))
+    cug = torch.from_numpy(cu).cuda()
+    o, l = fa.forward_varlen(qg, kg, vg, cug, max(lengths), causal=causal)
+    dq, dk, dv = fa.backward_varlen(qg, kg, vg, o, l, dog, cug, max(lengths), causal=causal)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    f64 = [x.to(torch.float64).numpy() for x in (q, k, v, do)]
+    oref, lref = VL.varlen_forward(f64[0], f64[1], f64[2], cu, scale, causal)
+    me, re_ = errs(o.cpu().numpy(), oref)
+    le, _ = errs(l.cpu().numpy(), lref)
+    say(f"  O max-abs {me:.3e} rel-L2 {re_:.3e}  L max-abs {le:.3e}")
+    assert me <= O_MAX and re_ <= O_REL and le <= L_MAX
+    gref = VL.varlen_backward(*f64, cu, scale, causal)
+    assert torch.isfinite(dq).all()
+    for name, x, ref in (("dK", dk, gref[1]), ("dV", dv, gref[2])):
+        ge, gr = errs(x.cpu().numpy(), ref)
+        top = max(1.0, float(np.abs(ref).max()))
+        say(f"  {name} max-abs {ge:.3e} (largest value {top:.2f}) rel-L2 {gr:.3e}")
+        assert ge <= G_MAX * top and gr <= G_REL, name
+
+
 def test_varlen_equal_lengths_match_the_dense_layout():
     """Equal-length packed sequences are the dense [B, H, N, d] problem with
     the batch moved into the token axis: the same kernels, the same numbers."""
