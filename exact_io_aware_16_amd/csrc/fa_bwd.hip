@@ -287,6 +287,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     return x;
   };
 
+  // The same addresses for steps whose buffer is known at compile time:
+  // per-lane constants with the XOR of each k-slice / head-dim block folded
+  // in (buffer 0), to which the buffer and row offsets add as immediates.
+  // dO gets its own constants (its offset would not fit the field).
+  uint32_t rq[NKK], rgo[NKK], tqd[NDB], tq1d[NDB], tgd[NDB], tg1d[NDB];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    rq[kk] = opaque(q_base0 + (row_lane ^ (uint32_t)(32 * kk)));
+    rgo[kk] = opaque(q_base0 + kDoutMinusQ + (row_lane ^ (uint32_t)(32 * kk)));
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    tqd[db] = opaque(q_base0 + (tq_lane ^ (uint32_t)(64 * db)));
+    tq1d[db] = opaque(q_base0 + ((tq_lane ^ 32u) ^ (uint32_t)(64 * db)));
+    tgd[db] = opaque(q_base0 + kDoutMinusQ + (tq_lane ^ (uint32_t)(64 * db)));
+    tg1d[db] = opaque(q_base0 + kDoutMinusQ + ((tq_lane ^ 32u) ^ (uint32_t)(64 * db)));
+  }
+  const uint32_t l2_lane = l2_base0 + (uint32_t)(32 * g);
+  auto step_ctx_c = [&](int st, auto buf) {
+    Step x;
+    x.qrow = x.tq = x.tq1 = 0u;  // not read on this path
+    x.l2 = l2_lane + (uint32_t)(decltype(buf)::value * kBQ * 4);
+    x.q0 = q_first + st * kBQ;
+    return x;
+  };
+
   // phase A group (query block qb, k-slice kk) and phase C group (qh = 2 qb + h,
   // head-dim block db): operand loads and products
   auto load_a = [&](const Step& x, int qb, int kk, bf16x8(&o)[2]) {
@@ -300,6 +326,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint32_t o1 = (x.tq1 ^ (uint32_t)(64 * db)) + rows + 8 * RB;
     o[0] = tr_pair(o0 + kDoutMinusQ, o1 + kDoutMinusQ);
     o[1] = tr_pair(o0, o1);
+  };
+  auto load_a_c = [&](auto buf, int qb, int kk, bf16x8(&o)[2]) {
+    constexpr uint32_t b = decltype(buf)::value * kTileBytes;
+    o[0] = lds_row16(rq[kk] + b + (uint32_t)(32 * qb * RB));
+    o[1] = lds_row16(rgo[kk] + b + (uint32_t)(32 * qb * RB));
+  };
+  auto load_c_c = [&](auto buf, int qh, int db, bf16x8(&o)[2]) {
+    constexpr uint32_t b = decltype(buf)::value * kTileBytes;
+    const uint32_t rows = b + (uint32_t)(16 * qh * RB);
+    o[0] = tr_pair(tgd[db] + rows, tg1d[db] + rows + 8 * RB);
+    o[1] = tr_pair(tqd[db] + rows, tq1d[db] + rows + 8 * RB);
   };
   auto mfma_a = [&](int qb, int kk, const bf16x8(&o)[2]) {
     s[qb] = mfma32(o[0], kres[kk], kk == 0 ? f32x16{} : s[qb]);
@@ -444,12 +481,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   // ---- steady state: A0(st+1) | C0(st) | A1(st+1) | C1(st), softmax(st, 1)
   // beside the first two phases and softmax(st+1, 0) beside the last two
-  auto iterate = [&](const Step& xc, const Step& xn, auto masked) {
+  // BUFC: buffer of step st's tile when known at compile time (else -1);
+  // step st+1's tile sits in the next one
+  auto iterate = [&](const Step& xc, const Step& xn, auto masked, auto bufc) {
+    constexpr int BUFC = decltype(bufc)::value;
     run(ic<4 * G>{},
         [&](auto gi, bf16x8(&o)[2]) {
           constexpr int n = decltype(gi)::value, ph = n / G, i = n % G;
-          if constexpr (ph == 0 || ph == 2) load_a(xn, ph >> 1, i, o);   // A0, A1 of step st+1
-          else load_c(xc, 2 * (ph >> 1) + i / NDB, i % NDB, o);          // C0, C1 of step st
+          if constexpr (BUFC >= 0) {
+            if constexpr (ph == 0 || ph == 2) load_a_c(ic<(BUFC + 1) % kTiles>{}, ph >> 1, i, o);
+            else load_c_c(ic<BUFC>{}, 2 * (ph >> 1) + i / NDB, i % NDB, o);
+          } else {
+            if constexpr (ph == 0 || ph == 2) load_a(xn, ph >> 1, i, o);   // A0, A1 of step st+1
+            else load_c(xc, 2 * (ph >> 1) + i / NDB, i % NDB, o);          // C0, C1 of step st
+          }
         },
         [&](auto gi, const bf16x8(&o)[2]) {
           constexpr int n = decltype(gi)::value, ph = n / G, i = n % G;
@@ -469,8 +514,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   auto step = [&](int st, auto masked) {
     __syncthreads();  // tile st+1 visible; every wave is done with tile st-1
     if (st + 2 < n_steps) issue_qtile((uint32_t)((st + 2) % kTiles), q_first + (st + 2) * kBQ);
-    iterate(step_ctx(st), step_ctx(st + 1), masked);
+    iterate(step_ctx(st), step_ctx(st + 1), masked, ic<-1>{});
     wait_loads();  // this wave's copies of tile st+2 have landed
+  };
+  // the same with step st's tile in buffer BUF (st % 3 == BUF)
+  auto step_c = [&](int st, auto buf) {
+    constexpr int BUF = decltype(buf)::value;
+    __syncthreads();
+    if (st + 2 < n_steps) issue_qtile((uint32_t)((BUF + 2) % kTiles), q_first + (st + 2) * kBQ);
+    iterate(step_ctx_c(st, buf), step_ctx_c(st + 1, ic<(BUF + 1) % kTiles>{}), no_masks, buf);
+    wait_loads();
   };
   // Steps that need masks form a prefix: the ones that meet the diagonal, or
   // all of them in the block that holds the end of the sequence.  Iteration
@@ -480,6 +533,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int n_mask = k0 + kBKV > N ? n_steps : CAUSAL ? min(n_steps, (k0 + kBKV - q_first + kBQ - 1) / kBQ) : 0;
   int st = 0;
   for (; st + 1 < n_steps && st < n_mask; ++st) step(st, with_masks);
+  // mask-free steps three at a time from a multiple of 3: tile st + i in buffer i
+  for (; st + 1 < n_steps && st % kTiles != 0; ++st) step(st, no_masks);
+  for (; st + 3 < n_steps; st += 3) {
+    step_c(st, ic<0>{});
+    step_c(st + 1, ic<1>{});
+    step_c(st + 2, ic<2>{});
+  }
   for (; st + 1 < n_steps; ++st) step(st, no_masks);
 
   // ---- last step: C0 with softmax(block 1) beside it, then C1

@@ -234,6 +234,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     x.key0 = t * BC;
     return x;
   };
+  // The same addresses for a loop whose buffers are known at compile time:
+  // per-lane constants with the XOR of each k-slice / head-dim block folded
+  // in (buffer 0), to which the buffer and row offsets add as immediates.
+  // V rows get their own constants (their offset would not fit the field).
+  uint32_t rlk[NKK], rlv[NKK], tkd[NDB], tk1d[NDB];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    rlk[kk] = opaque(k_base0 + (row_lane ^ (uint32_t)(32 * kk)));
+    rlv[kk] = opaque(k_base0 + kVMinusK + (row_lane ^ (uint32_t)(32 * kk)));
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    tkd[db] = opaque(k_base0 + (tk_lane ^ (uint32_t)(64 * db)));
+    tk1d[db] = opaque(k_base0 + ((tk_lane ^ 32u) ^ (uint32_t)(64 * db)));
+  }
 
   // score group (key block kb, k-slice kk) and dQ group (kh = 2 kb + h,
   // head-dim blocks 2 pr, 2 pr + 1): operand loads and products
@@ -248,6 +263,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     for (int y = 0; y < 2; ++y) {
       const int db = 2 * pr + y;
       o[y] = tr_pair((x.tk ^ (uint32_t)(64 * db)) + rows, (x.tk1 ^ (uint32_t)(64 * db)) + rows + 8 * RB);
+    }
+  };
+  auto load_s_c = [&](auto buf, int kb, int kk, bf16x8(&o)[2]) {
+    constexpr uint32_t b = decltype(buf)::value * kTileBytes;
+    o[0] = lds_row16(rlk[kk] + b + (uint32_t)(32 * kb * RB));
+    o[1] = lds_row16(rlv[kk] + b + (uint32_t)(32 * kb * RB));
+  };
+  auto load_q_c = [&](auto buf, int kh, int pr, bf16x8(&o)[2]) {
+    constexpr uint32_t b = decltype(buf)::value * kTileBytes;
+    const uint32_t rows = b + (uint32_t)(16 * kh * RB);
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int db = 2 * pr + y;
+      o[y] = tr_pair(tkd[db] + rows, tk1d[db] + rows + 8 * RB);
     }
   };
   auto mfma_s = [&](int kb, int kk, const bf16x8(&o)[2]) {
@@ -352,12 +381,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   wait_loads();  // this wave's copies of tile 1 have landed
 
   // ---- steady state: S(t+1, kb) | Q(t, kb) for every block kb
-  auto iterate = [&](const Tile& xc, const Tile& xn, auto masked) {
+  // BUFC: buffer of tile t when known at compile time (else -1); tile t+1
+  // sits in the next one
+  auto iterate = [&](const Tile& xc, const Tile& xn, auto masked, auto bufc) {
+    constexpr int BUFC = decltype(bufc)::value;
     run(ic<NKB * GP>{},
         [&](auto gi, bf16x8(&o)[2]) {
           constexpr int n = decltype(gi)::value, kb = n / GP, i = n % GP;
-          if constexpr (i < GS) load_s(xn, kb, i, o);
-          else load_q(xc, q_kh(kb, i - GS), q_pr(i - GS), o);
+          if constexpr (BUFC >= 0) {
+            if constexpr (i < GS) load_s_c(ic<(BUFC + 1) % kTiles>{}, kb, i, o);
+            else load_q_c(ic<BUFC>{}, q_kh(kb, i - GS), q_pr(i - GS), o);
+          } else {
+            if constexpr (i < GS) load_s(xn, kb, i, o);
+            else load_q(xc, q_kh(kb, i - GS), q_pr(i - GS), o);
+          }
         },
         [&](auto gi, const bf16x8(&o)[2]) {
           constexpr int n = decltype(gi)::value, kb = n / GP, i = n % GP;
@@ -376,14 +413,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   auto step = [&](int t, auto masked) {
     __syncthreads();  // tile t+1 visible; every wave is done with tile t-1
     if (t + 2 < n_tiles) issue_tile((uint32_t)((t + 2) % kTiles), (t + 2) * BC);
-    iterate(tile_ctx(t), tile_ctx(t + 1), masked);
+    iterate(tile_ctx(t), tile_ctx(t + 1), masked, ic<-1>{});
     wait_loads();  // this wave's copies of tile t+2 have landed
+  };
+  // the same with tile t in buffer BUFC (t % 3 == BUFC)
+  auto step_c = [&](int t, auto bufc) {
+    __syncthreads();
+    if (t + 2 < n_tiles) issue_tile((uint32_t)((decltype(bufc)::value + 2) % kTiles), (t + 2) * BC);
+    Tile xc, xn;  // only key0 is read
+    xc.key0 = t * BC;
+    xn.key0 = (t + 1) * BC;
+    iterate(xc, xn, no_masks, bufc);
+    wait_loads();
   };
   // Tiles that need masks (for any row of the workgroup) form a suffix: the
   // ones that meet the diagonal and the one holding the end of the sequence.
   // Iteration t touches tiles t and t+1, so it needs masks iff t+1 >= t_mask.
   const int t_mask = min(CAUSAL ? (q_start + 1) / BC : n_tiles, N / BC);
   int t = 0;
+  // mask-free tiles three at a time from t = 0: tile t + i in buffer i
+  for (; t + 3 < n_tiles && t + 3 < t_mask; t += 3) {
+    step_c(t, ic<0>{});
+    step_c(t + 1, ic<1>{});
+    step_c(t + 2, ic<2>{});
+  }
   for (; t + 1 < n_tiles && t + 1 < t_mask; ++t) step(t, no_masks);
   for (; t + 1 < n_tiles; ++t) step(t, with_masks);
 

@@ -75,7 +75,10 @@ constexpr int kComputeUnits = 256;
 template <int SPLIT>
 struct Smem {
   bf16_raw k[SPLIT][kKSlots][kBC * kD];
-  bf16_raw v[SPLIT][2][kBC * kDV];
+  // V ring: three slots with one key range (slots known at compile time in
+  // the three-tile loop), two with two ranges (LDS holds no more)
+  static constexpr int kVSlots = SPLIT == 1 ? 3 : 2;
+  bf16_raw v[SPLIT][kVSlots][kBC * kDV];
 };
 
 // LDS tile layout (16-byte slots, XOR swizzle, no padding):
@@ -150,8 +153,8 @@ struct Wave {
   Half hs[2];
   float part[2][4];          // piece sums of the sub-tile in progress, per half
   float pf[2][2][8];         // float32 weights before packing, [half][16-key group]
-  int kaddr[kNKK];
-  int vaddr[kNDB];
+  uint32_t kaddr[kNKK];       // LDS byte address of this lane's K operand row in slot 0 of the ring
+  uint32_t vaddr[kNDB];       // same for the V^T transpose reads
   float c;                    // |scale| log2(e)
   int last_key[2];            // highest visible key per half row (causal: the row; always < Nk)
 
@@ -350,11 +353,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_r64_kernel(
   bf16_raw(*vs_s)[kBC * kDV] = sm.v[kr];
   constexpr uint32_t kTileBytes = kBC * kD * 2, vTileBytes = kBC * kDV * 2, kSubBytes = kSub * kD * 2;
   // K sub-tile t of the range sits in slot (t / 2) % 3, rows 32 (t % 2) ..
+  // (byte offsets from the ring's first slot; the lane's operand addresses
+  // carry the ring base)
+  constexpr int kVSlots = Smem<SPLIT>::kVSlots;
   auto ksub_addr = [&](int t) {
-    return Wave::opaque(kring + (uint32_t)((t >> 1) % kKSlots) * kTileBytes + (uint32_t)(t & 1) * kSubBytes);
+    return Wave::opaque((uint32_t)((t >> 1) % kKSlots) * kTileBytes + (uint32_t)(t & 1) * kSubBytes);
   };
   auto vsub_addr = [&](int t) {
-    return Wave::opaque(vring + (uint32_t)((t >> 1) & 1) * vTileBytes + (uint32_t)(t & 1) * kSubBytes);
+    return Wave::opaque((uint32_t)((t >> 1) % kVSlots) * vTileBytes + (uint32_t)(t & 1) * kSubBytes);
   };
 
   // prologue copies: K(0), V(0), K(1) of the range
@@ -386,14 +392,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_r64_kernel(
     w.hs[h] = Half{-INFINITY, 0.f, 0.f};
   }
 #pragma unroll
-  for (int kk = 0; kk < kNKK; ++kk) w.kaddr[kk] = col * kD * 2 + 16 * ((2 * kk + g) ^ kswz(col));
+  for (int kk = 0; kk < kNKK; ++kk) w.kaddr[kk] = kring + (uint32_t)(col * kD * 2 + 16 * ((2 * kk + g) ^ kswz(col)));
   {
     const int grp = lane >> 4, sl = lane & 15;
 #pragma unroll
     for (int db = 0; db < kNDB; ++db) {
       const int krow = 8 * (grp >> 1) + (sl >> 2);
       const int d = 32 * db + 16 * (grp & 1) + 4 * (sl & 3);
-      w.vaddr[db] = krow * kDV * 2 + 16 * ((d >> 3) ^ vswz(krow)) + 2 * (d & 7);
+      w.vaddr[db] = vring + (uint32_t)(krow * kDV * 2 + 16 * ((d >> 3) ^ vswz(krow)) + 2 * (d & 7));
     }
   }
 #pragma unroll
@@ -455,20 +461,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_r64_kernel(
       __syncthreads();
       if (ra + u + 2 < rb)
         issue_tile<RG, true>(ks_s[(u + 2) % kKSlots], Kh, Nk, key_a + (u + 2) * kBC, k_row, cp, rg);
-      if (ra + u + 1 < rb) issue_tile<RG, false>(vs_s[(u + 1) & 1], Vh, Nk, key_a + (u + 1) * kBC, v_row, cp, rg);
+      if (ra + u + 1 < rb)
+        issue_tile<RG, false>(vs_s[(u + 1) % kVSlots], Vh, Nk, key_a + (u + 1) * kBC, v_row, cp, rg);
     };
     // Steady state, two sub-tiles (one LDS tile) per iteration: every
     // sub-tile involved is mask-free and the next one exists.  Slices 0, 1 of
     // sub-tile v + 2 are loaded ahead even when it does not exist (an in-range
     // LDS read whose value is never used).
-    auto fast_step = [&](auto P, int v) {
+    auto fast_step_at = [&](auto P, uint32_t k_next, uint32_t v_cur, uint32_t k_after) {
       constexpr int pc = decltype(P)::value, pn = 1 - pc;
-      w.template phase1<true, true>(pc, pn, ksub_addr(v + 1), vsub_addr(v));
+      w.template phase1<true, true>(pc, pn, k_next, v_cur);
       w.commit(1);
-      w.template phase2<true, true>(pc, pn, vsub_addr(v), ksub_addr(v + 2));
+      w.template phase2<true, true>(pc, pn, v_cur, k_after);
       w.commit(0);
     };
+    auto fast_step = [&](auto P, int v) { fast_step_at(P, ksub_addr(v + 1), vsub_addr(v), ksub_addr(v + 2)); };
     int u = 0;
+    if constexpr (SPLIT == 1) {
+      // Three LDS tiles per iteration from u = 0: tile u + i sits in slot i
+      // of both rings, so every operand address is a lane register plus an
+      // immediate offset (no address arithmetic in the loop).
+      constexpr auto koff = [](int j) { return (uint32_t)(((j >> 1) % 3) * (int)kTileBytes + (j & 1) * (int)kSubBytes); };
+      constexpr auto voff = [](int j) { return (uint32_t)(((j >> 1) % 3) * (int)vTileBytes + (j & 1) * (int)kSubBytes); };
+      for (; 2 * u + 6 < n_clean; u += 3) {
+        static_for<0, 3>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          top(u + i);
+          fast_step_at(ic<0>{}, koff(2 * i + 1), voff(2 * i), koff(2 * i + 2));
+          fast_step_at(ic<1>{}, koff(2 * i + 2), voff(2 * i + 1), koff(2 * i + 3));
+        });
+      }
+    }
     for (; 2 * u + 2 < n_clean; ++u) {
       top(u);
       fast_step(ic<0>{}, 2 * u);
