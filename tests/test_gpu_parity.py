@@ -326,6 +326,21 @@ def test_fwd_long_causal_sampled_rows(w):
     check_fwd(og, lg, oref, lref, w.name)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_long_ragged_sampled_rows(causal):
+    """B1 H2 N = 40013, d = 128: a key count that is no multiple of a tile,
+    long enough for the three-tile steady loop, the one-tile loop and the
+    masked tail to all run; 128 seeded rows of each head against the oracle."""
+    w = I.Workload("fwd_long_ragged", 1300 + int(causal), 1, 2, 40013, 128, causal, "bf16")
+    t = I.make_inputs(w)
+    o, l = run_fwd(t, causal)
+    rows = lambda b, h: I.sample_rows(w.N, 128, 1300 + 10 * int(causal) + h)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(128), rows=rows)
+    og = np.stack([np.stack([o[b, h][rows(b, h)] for h in range(w.H)]) for b in range(w.B)])
+    lg = np.stack([np.stack([l[b, h][rows(b, h)] for h in range(w.H)]) for b in range(w.B)])
+    check_fwd(og, lg, oref, lref, f"long ragged N={w.N} causal={causal}")
+
+
 # ------------------------------------------------------------------ invariants and edge cases
 def test_fwd_uniform_scores_give_mean_of_values():
     """Q = 0: every visible key has weight 1/count (closed form)."""
