@@ -33,9 +33,12 @@
 //                     beside the weights of sub-tile u, half 1;
 //   step u, phase 2:  O^T += V(u)^T P(u)^T for both halves (16 products)
 //                     beside the weights of sub-tile u+1, half 0.
-// The vector instructions of each weight piece sit between the products in
-// program order (sched_group_barrier), so a lone wave issues them while its
-// products run.  K runs one tile ahead of V in the LDS rings.
+// The weights go in pieces of two per lane, one piece per group of two
+// products (phase 2's first group reads no S of the next sub-tile, so its
+// second group takes two pieces); sched_group_barrier keeps each piece's
+// vector instructions between the products in program order, so a lone wave
+// issues them while its products run.  K runs one tile ahead of V in the LDS
+// rings.
 //
 // Register plan per wave (one wave per SIMD, up to 512 registers): Q as the
 // B operand of S^T (16 x 4 registers), O^T accumulators 2 x 4 blocks of
@@ -151,7 +154,7 @@ struct Wave {
   bf16x8 ak[3];               // K operand ring: slice kk in slot kk % 3
   bf16x8 av[3];               // V^T operand ring: group gi in slot gi % 3
   Half hs[2];
-  float part[2][4];          // piece sums of the sub-tile in progress, per half
+  float part[2][8];          // piece sums of the sub-tile in progress, per half
   float pf[2][2][8];         // float32 weights before packing, [half][16-key group]
   uint32_t kaddr[kNKK];       // LDS byte address of this lane's K operand row in slot 0 of the ring
   uint32_t vaddr[kNDB];       // same for the V^T transpose reads
@@ -181,19 +184,26 @@ struct Wave {
       for (int e = 0; e < 8; ++e) s[p][h][8 * hh + e] = e > lim ? -INFINITY : s[p][h][8 * hh + e];
     }
   }
-  // Weight piece q (0 .. 3) of half h of the sub-tile of parity p: four
-  // weights against the current reference, their sum; pieces 1 and 3 pack
-  // their 16-key group to bf16.
+  // Weight piece q (0 .. 7) of half h of the sub-tile of parity p: two
+  // weights against the current reference and their sum; pieces 3 and 7
+  // pack their 16-key group to bf16.  The empty asm keeps the sum where it
+  // is computed: nothing in the loop reads it before commit(), and the
+  // compiler otherwise sinks every piece's add past the loop's tile branches
+  // into one burst of vector work with no product beside it.
   __device__ __forceinline__ void piece(int p, int h, int q) {
-    const int kg = q >> 1, e0 = 4 * (q & 1);
+    const int kg = q >> 2, e0 = 2 * (q & 3);
 #pragma unroll
-    for (int e = e0; e < e0 + 4; ++e) pf[h][kg][e] = fast_exp2(fmaf(s[p][h][8 * kg + e], c, -hs[h].m_use));
-    part[h][q] = (pf[h][kg][e0] + pf[h][kg][e0 + 1]) + (pf[h][kg][e0 + 2] + pf[h][kg][e0 + 3]);
-    if (q & 1) pb[p][h][kg] = pack_bf16x8(pf[h][kg]);
+    for (int e = e0; e < e0 + 2; ++e) pf[h][kg][e] = fast_exp2(fmaf(s[p][h][8 * kg + e], c, -hs[h].m_use));
+    part[h][q] = pf[h][kg][e0] + pf[h][kg][e0 + 1];
+    asm volatile("" : "+v"(part[h][q]));
+    if ((q & 3) == 3) pb[p][h][kg] = pack_bf16x8(pf[h][kg]);
   }
-  // The sub-tile's weights join the running sum.
+  // The sub-tile's weights join the running sum (pairs, then pairs of
+  // pairs: four weights, eight, sixteen).
   __device__ __forceinline__ void commit(int h) {
-    hs[h].l += (part[h][0] + part[h][1]) + (part[h][2] + part[h][3]);
+    hs[h].l += ((part[h][0] + part[h][1]) + (part[h][2] + part[h][3])) +
+               ((part[h][4] + part[h][5]) + (part[h][6] + part[h][7]));
+    asm volatile("" : "+v"(hs[h].l));
   }
   // The reference of half h: the exact row max of the (masked) sub-tile of
   // parity p.
@@ -207,7 +217,7 @@ struct Wave {
   }
   // The weights of one half outside the pipelined phases.
   __device__ __forceinline__ void softmax(int p, int h) {
-    static_for<0, 4>([&](auto Q) { piece(p, h, decltype(Q)::value); });
+    static_for<0, 8>([&](auto Q) { piece(p, h, decltype(Q)::value); });
     commit(h);
   }
 
@@ -227,7 +237,7 @@ struct Wave {
   // of it already loaded) beside the softmax of (current sub-tile, half 1).
   // Group kk: the two products of slice kk (one per half) share one K
   // operand; slice kk + 2 loads between them, into the slot group kk - 1
-  // read.  LOAD_V: the first two V^T operands of phase 2 load in the last
+  // read; weight piece kk follows.  LOAD_V: the first two V^T operands of phase 2 load in the last
   // groups.  The product before the phase read av[1] and pb[pn][1][1] (the
   // last product of phase 2).
   template <bool WITH_SOFT, bool LOAD_V>
@@ -241,7 +251,7 @@ struct Wave {
       if constexpr (LOAD_V && kk >= kNKK - 2) load_v(kk - (kNKK - 2), vsub);
       s[pn][1] = mfma32(ak[kk % 3], qf[1][kk], kk == 0 ? f32x16{} : s[pn][1]);
       anchor(s[pn][1]);
-      if constexpr (WITH_SOFT && kk % 2 == 0) piece(pc, 1, kk / 2);
+      if constexpr (WITH_SOFT) piece(pc, 1, kk);
       sg<kSgMfma, 1>(); sg<kSgDsRead, 2>(); sg<kSgValu, 4>(); sg<kSgMfma, 1>(); sg<kSgValu, 30>();
       group_fence();
     });
@@ -250,7 +260,9 @@ struct Wave {
   // Phase 2: O^T += V^T P^T of the current sub-tile (both halves; groups 0
   // and 1 already loaded) beside the softmax of (next sub-tile, half 0).
   // Group gi: row block gi % 4 of 16-key group gi / 4, two products (one per
-  // half) sharing one V^T operand; group gi + 2 loads between them.  NEXT_K:
+  // half) sharing one V^T operand; group gi + 2 loads between them; weight
+  // pieces 0 and 1 follow group 1, piece gi follows group gi >= 2 (S of the
+  // next sub-tile is not read right after its last product).  NEXT_K:
   // slices 0 and 1 of the sub-tile after next load in the last groups.  The
   // product before the phase read ak[1] (and Q).
   template <bool WITH_SOFT, bool NEXT_K>
@@ -265,7 +277,11 @@ struct Wave {
       if constexpr (NEXT_K && gi >= 2 * kNDB - 2) load_k(gi - (2 * kNDB - 2), knext);
       o[1][db] = mfma32(av[gi % 3], pb[pc][1][kg], o[1][db]);
       after(o[1][db], pb[pc][0][kg]);
-      if constexpr (WITH_SOFT && gi % 2 == 1) piece(pn, 0, gi / 2);
+      if constexpr (WITH_SOFT && gi == 1) {
+        piece(pn, 0, 0);
+        piece(pn, 0, 1);
+      }
+      if constexpr (WITH_SOFT && gi >= 2) piece(pn, 0, gi);
       sg<kSgMfma, 1>(); sg<kSgDsRead, 2>(); sg<kSgValu, 4>(); sg<kSgMfma, 1>(); sg<kSgValu, 30>();
       group_fence();
     });
