@@ -1,19 +1,25 @@
 // Exact attention forward, bf16 inputs, float32 outputs, gfx950 matrix cores.
 //
-// Follows the blocked recurrence of "From softmax to attention: rescale the
-// output too" (FlashAttention: The Matrix You Never Have to Write Down):
-// per query row a running max m, running sum l and unnormalised output O;
-// a key tile whose scores exceed m moves the reference to m_new and scales
-// l and O by e^(m - m_new); the tile's terms are added; O is divided by l
-// once after the last tile.  Scores never leave the chip.
+// The blocked computation of "From softmax to attention: rescale the output
+// too" (FlashAttention: The Matrix You Never Have to Write Down): per query
+// row a running sum l and unnormalised output O over the key tiles, both
+// against a reference m, and one division of O by l after the last tile.
+// Scores never leave the chip.
 //
-// Rescale policy: the reference m only moves when a tile's row max exceeds
-// it by more than kRescaleSlack (log2 units) for some row of the wave, as in
-// the deferred correction described under "What it doesn't solve" (FA4
-// paragraph) of the same page.  Until then the tile's exponentials are taken
-// against the old reference (values up to 2^kRescaleSlack), l and O stay in
-// one consistent frame, and the final O / l and L = m + log l are the same
-// function -- only the rounding differs.
+// Reference of the exponentials: any common reference per row gives the same
+// O / l and L = m + log l (the identity the recurrence rests on); the max
+// only keeps the terms in range.  The FA4 paragraph under "What it doesn't
+// solve" on the same page defers the rescale until the max has moved far;
+// this kernel defers it to the end.  Each row's reference is the exact max
+// of the first key tile its wave computes and never moves: no per-tile max,
+// no rescale.  Later weights may exceed 1; float32 holds them unless a
+// weight, a sum or an O element overflows, and a check after the loop sees
+// exactly that (a non-finite value).  Then the workgroup runs again with the
+// exact row max over all of its keys as the reference (a pass over K in
+// global memory), the page's own frame, in which no weight exceeds 1.  A
+// row's visible keys are a prefix of the range (the causal mask and the end
+// of the sequence only hide later keys), so a row that sees nothing in its
+// wave's first tile sees nothing at all.
 //
 // Contract (the first page's flash_attention, "Build it"): Q [Nq, d],
 // K [Nk, d], V [Nk, dv] per head; O [Nq, dv]; upper-left causal masking
@@ -55,7 +61,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;        // query rows per workgroup
 constexpr int kComputeUnits = 256;      // MI355X
-constexpr float kRescaleSlack = 8.0f;   // log2 units: P <= 256 before a forced rescale
 
 // keys per tile: 128 when both widths are 64, else 64 (two buffers of K and V
 // per key range fit in 64 KiB either way)
@@ -296,7 +301,10 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   // then scalar arithmetic
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   // prologue loads: first K and V tile of the range
-  if (t_first < t_end) issue_tiles<D, DV>(sm.k[half][0], sm.v[half][0], Kh, Vh, Nk, t_first * BC, tc, wave_s);
+  auto first_copies = [&]() {
+    if (t_first < t_end) issue_tiles<D, DV>(sm.k[half][0], sm.v[half][0], Kh, Vh, Nk, t_first * BC, tc, wave_s);
+  };
+  first_copies();
 
   // loop-invariant lane parts of the LDS operand addresses (bytes)
   int kaddr[NKK];
@@ -330,10 +338,6 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   }
 
   f32x16 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_ref = -INFINITY, l_run = 0.f, l_rnd = 0.f;
 
   // operand register sets (see pin()): K operands of the score product and
@@ -350,141 +354,205 @@ __global__ __launch_bounds__(kThreads * SPLIT, SPLIT == 1 ? 2 : 1) void fwd_bf16
   }
 
   f32x16 s_cur[NKB];
-  for (int it = 0; it < n_iter; ++it) {
-    const int t = t_first + it;
-    const int key0 = t * BC;
-    // K(t) and V(t) have landed (own loads) and are visible (barrier); every
-    // wave is done with tile t-1, whose buffers refill now with tile t+1.
-    wait_tile_loads();
-    __syncthreads();
-    if (t >= t_end) continue;  // the shorter key range idles through the barriers
-    if (t + 1 < t_end)
-      issue_tiles<D, DV>(sm.k[half][(it + 1) & 1], sm.v[half][(it + 1) & 1], Kh, Vh, Nk, key0 + BC, tc, wave_s);
-    // a wave whose 32 rows all lie past the last query (few query rows, as in
-    // decoding, or the ragged last block), or (causal) before the tile's
-    // first key, only helps copy the tiles
-    if (q0w >= Nq || (CAUSAL && key0 > q0w + 31)) continue;
-    tile_scores<D, BC>(s_cur, reinterpret_cast<const char*>(sm.k[half][it & 1]), kaddr, qf, ak);
+  // One pass over the key tiles.  exact_ref: the reference is already set
+  // (the exact max over the range); otherwise each wave's first tile sets it.
+  auto run_pass = [&](bool exact_ref) {
+    bool ref_set = exact_ref;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    l_run = 0.f;
+    l_rnd = 0.f;
+    for (int it = 0; it < n_iter; ++it) {
+      const int t = t_first + it;
+      const int key0 = t * BC;
+      // K(t) and V(t) have landed (own loads) and are visible (barrier); every
+      // wave is done with tile t-1, whose buffers refill now with tile t+1.
+      wait_tile_loads();
+      __syncthreads();
+      if (t >= t_end) continue;  // the shorter key range idles through the barriers
+      if (t + 1 < t_end)
+        issue_tiles<D, DV>(sm.k[half][(it + 1) & 1], sm.v[half][(it + 1) & 1], Kh, Vh, Nk, key0 + BC, tc, wave_s);
+      // a wave whose 32 rows all lie past the last query (few query rows, as in
+      // decoding, or the ragged last block), or (causal) before the tile's
+      // first key, only helps copy the tiles
+      if (q0w >= Nq || (CAUSAL && key0 > q0w + 31)) continue;
+      tile_scores<D, BC>(s_cur, reinterpret_cast<const char*>(sm.k[half][it & 1]), kaddr, qf, ak);
 
-    const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > Nk;
-    if (need_mask) {
-      // register 8 h + e of half g holds key key0 + 32 kb + 16 h + 8 g + e;
-      // keys above last_key (causal: the row; always: Nk - 1) are masked
-      const int last_key = CAUSAL ? min(my_q, Nk - 1) : Nk - 1;
+      const bool need_mask = (CAUSAL && key0 + BC - 1 > q0w) || key0 + BC > Nk;
+      if (need_mask) {
+        // register 8 h + e of half g holds key key0 + 32 kb + 16 h + 8 g + e;
+        // keys above last_key (causal: the row; always: Nk - 1) are masked
+        const int last_key = CAUSAL ? min(my_q, Nk - 1) : Nk - 1;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int lim = last_key - (key0 + 32 * kb + 16 * h + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_cur[kb][8 * h + e] = e > lim ? -INFINITY : s_cur[kb][8 * h + e];
+          }
+      }
+      // the first tile this wave computes sets the reference: its exact row max
+      // (both lane halves), in log2 units; -inf for a row that sees no key
+      if (!ref_set) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
+        m_ref = halves_max(mx) * c;
+        ref_set = true;
+      }
+      // every score product of tile t has completed once mx exists (products
+      // complete in order): so have all earlier products, and the K and V^T
+      // operand sets of this and the previous tile may be reused
+      float mx = s_cur[0][15];
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb) mx += s_cur[kb][15];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) pin(ak[j][kb], mx);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) pin(av[j][db], mx);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        pin(pb[kb][0], mx);
+        pin(pb[kb][1], mx);
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;  // row with nothing visible yet
+
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        // dropout mask words of this 32-key block: dm[x] is this row's word of
+        // the 4 x 4 block holding keys 16 (x / 2) + 8 g + 4 (x % 2) .. + 3 (lane
+        // x of the 4-lane group computes that block)
+        uint32_t dm[4];
+        if constexpr (DROP) {
+          const int qd = col & 3;
+          uint32_t w[4] = {(uint32_t)(key0 + 32 * kb + 16 * (qd >> 1) + 8 * g + 4 * (qd & 1)) >> 2,
+                           (uint32_t)my_q >> 2, (uint32_t)bh, dp.offset};
+          philox4x32_10(w, dp.k0, dp.k1);
+          quad_transpose(w, dm, qd);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = fast_exp2(fmaf(s_cur[kb][8 * h + e], c, -m_use));
+            l_run += p[e];
+          }
+          pb[kb][h] = pack_bf16x8(p);
+          // l_rnd sums the bf16-rounded weights that actually multiply V, so O
+          // is normalised by exactly the weights applied (a dominant weight's
+          // rounding cancels in O / l_rnd); l_run (exact terms) gives L.  With
+          // dropout both sums cover every weight; only the product with V
+          // loses the dropped ones.
+          l_rnd = sum_bf16x8(pb[kb][h], l_rnd);
+          if constexpr (DROP) pb[kb][h] = drop_bf16x8(pb[kb][h], dm[2 * h], dm[2 * h + 1], dp.t);
+        }
+      }
+
+      // O^T += V^T P^T, V^T operand via transpose reads of the row-major tile;
+      // operand sets rotate per (key block, half) group
+      const char* vtile = reinterpret_cast<const char*>(sm.v[half][it & 1]);
+      // the other wave on this SIMD is usually in its softmax here: raised
+      // issue priority keeps the matrix core fed through this product
+      // (measured 2% on the forward workloads)
+      __builtin_amdgcn_s_setprio(2);
+      // V^T operands of group gi = (key block gi / 2, half gi % 2) into set gi % 2
+      auto load_v = [&](int gi) {
+        const int kb = gi >> 1, h = gi & 1;
+        bf16x8(&a)[NDB] = av[gi & 1];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          v4i16 part[2];
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr)
+            part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(vtile + vaddr[db] + (32 * kb + 16 * h + 4 * rr) * DV * 2));
+          a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      };
+      // the next group's operands load while this group's products run
+      load_v(0);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int lim = last_key - (key0 + 32 * kb + 16 * h + 8 * g);
+          const int grp_i = 2 * kb + h;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s_cur[kb][8 * h + e] = e > lim ? -INFINITY : s_cur[kb][8 * h + e];
+          for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(av[grp_i & 1][db], pb[kb][h], oacc[db]);
+          group_fence();
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) pin(av[(grp_i + 1) & 1][db]);
+          if (grp_i > 0) pin(pb[(grp_i - 1) >> 1][(grp_i - 1) & 1]);
+          if (grp_i + 1 < 2 * NKB) load_v(grp_i + 1);
         }
+      __builtin_amdgcn_s_setprio(0);
     }
-    // tile row max (both lane halves), in log2 units
+  };
+  run_pass(false);
+  // The check: a non-finite running sum or O element in any wave of the
+  // workgroup runs the pass again against the exact row max.
+  do {
+    float tot = l_run + l_rnd;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tot += oacc[db][i];
+    const bool bad = __any(!(fabsf(tot) <= 3.0e38f));
+    // the flags go through the first K buffer once every wave is done with it
+    int* redo = reinterpret_cast<int*>(&sm.k[0][0][0]);
+    __syncthreads();
+    if (lane == 0) redo[tid >> 6] = bad ? 1 : 0;
+    __syncthreads();
+    int any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves * SPLIT; ++w) any_bad |= redo[w];
+    if (!__builtin_amdgcn_readfirstlane(any_bad)) break;
+
+    // The exact row max over the wave's tiles, S recomputed from K in global
+    // memory (rows in the order the LDS tiles hold them, so the register
+    // layout and the masks are those of the loop).
     float mx = -INFINITY;
+    if (q0w < Nq) {
+      const int last_key = CAUSAL ? min(my_q, Nk - 1) : Nk - 1;
+      for (int t = t_first; t < t_end; ++t) {
+        const int key0 = t * BC;
+        if (CAUSAL && key0 > q0w + 31) break;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int key = min(key0 + 32 * kb + perm32(col), Nk - 1);
+          const bf16_raw* kp = Kh + (size_t)key * k_stride + 8 * g;
+          bf16x8 kf[NKK];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
-    mx = halves_max(mx) * c;
-    // the scores of tile t are consumed: every MFMA issued before the row max
-    // (all K and V^T operand sets of this and the previous tile) has run
+          for (int kk = 0; kk < NKK; ++kk) kf[kk] = as_bf16x8(ld16(kp + 16 * kk));
+          f32x16 a{};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+          for (int kk = 0; kk < NKK; ++kk) a = mfma32(kf[kk], qf[kk], a);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) pin(ak[j][kb], mx);
+          for (int h = 0; h < 2; ++h) {
+            const int lim = last_key - (key0 + 32 * kb + 16 * h + 8 * g);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) pin(av[j][db], mx);
-    }
+            for (int e = 0; e < 8; ++e) mx = e > lim ? mx : fmaxf(mx, a[8 * h + e]);
+          }
+          // the products have completed (their results are read) before the
+          // next block's loads reuse the operand registers
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      pin(pb[kb][0], mx);
-      pin(pb[kb][1], mx);
-    }
-    if (__any(mx > m_ref + kRescaleSlack)) {
-      const float m_new = fmaxf(m_ref, mx);
-      // 0 while nothing was accumulated; a row with nothing visible keeps its (zero) sums
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
-      l_rnd *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;  // row with nothing visible yet
-
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      // dropout mask words of this 32-key block: dm[x] is this row's word of
-      // the 4 x 4 block holding keys 16 (x / 2) + 8 g + 4 (x % 2) .. + 3 (lane
-      // x of the 4-lane group computes that block)
-      uint32_t dm[4];
-      if constexpr (DROP) {
-        const int qd = col & 3;
-        uint32_t w[4] = {(uint32_t)(key0 + 32 * kb + 16 * (qd >> 1) + 8 * g + 4 * (qd & 1)) >> 2,
-                         (uint32_t)my_q >> 2, (uint32_t)bh, dp.offset};
-        philox4x32_10(w, dp.k0, dp.k1);
-        quad_transpose(w, dm, qd);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(s_cur[kb][8 * h + e], c, -m_use));
-          l_run += p[e];
+          for (int kk = 0; kk < NKK; ++kk) pin(kf[kk], mx);
         }
-        pb[kb][h] = pack_bf16x8(p);
-        // l_rnd sums the bf16-rounded weights that actually multiply V, so O
-        // is normalised by exactly the weights applied (a dominant weight's
-        // rounding cancels in O / l_rnd); l_run (exact terms) gives L.  With
-        // dropout both sums cover every weight; only the product with V
-        // loses the dropped ones.
-        l_rnd = sum_bf16x8(pb[kb][h], l_rnd);
-        if constexpr (DROP) pb[kb][h] = drop_bf16x8(pb[kb][h], dm[2 * h], dm[2 * h + 1], dp.t);
       }
     }
-
-    // O^T += V^T P^T, V^T operand via transpose reads of the row-major tile;
-    // operand sets rotate per (key block, half) group
-    const char* vtile = reinterpret_cast<const char*>(sm.v[half][it & 1]);
-    // the other wave on this SIMD is usually in its softmax here: raised
-    // issue priority keeps the matrix core fed through this product
-    // (measured 2% on the forward workloads)
-    __builtin_amdgcn_s_setprio(2);
-    // V^T operands of group gi = (key block gi / 2, half gi % 2) into set gi % 2
-    auto load_v = [&](int gi) {
-      const int kb = gi >> 1, h = gi & 1;
-      bf16x8(&a)[NDB] = av[gi & 1];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        v4i16 part[2];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-          part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(vtile + vaddr[db] + (32 * kb + 16 * h + 4 * rr) * DV * 2));
-        a[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
-    // the next group's operands load while this group's products run
-    load_v(0);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int grp_i = 2 * kb + h;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(av[grp_i & 1][db], pb[kb][h], oacc[db]);
-        group_fence();
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) pin(av[(grp_i + 1) & 1][db]);
-        if (grp_i > 0) pin(pb[(grp_i - 1) >> 1][(grp_i - 1) & 1]);
-        if (grp_i + 1 < 2 * NKB) load_v(grp_i + 1);
-      }
-    __builtin_amdgcn_s_setprio(0);
-  }
+    m_ref = halves_max(mx) * c;
+    __syncthreads();  // every wave has read the flags before the tiles refill
+    first_copies();
+    run_pass(true);
+  } while (false);
 
   if constexpr (SPLIT == 2) {
     // merge the second key range into the first: with m = max(m0, m1),

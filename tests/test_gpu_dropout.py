@@ -125,6 +125,32 @@ def test_dropout_in_the_large_grid_launch():
         say(f"  head ({b},{h}) O max-abs {me:.3e}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_dropout_forward_rising_scores(d, causal):
+    """Every query all ones and keys rising by about 400 base-2 units along
+    the sequence: against a reference from the first key tile the weights
+    leave float32, and the forward restarts against the exact row max.  The
+    regenerated mask of the restart is the same, so O and L match the
+    dropout oracle."""
+    B, H, N, p, seed = 1, 2, 1200, 0.2, 4242
+    c = (1 / math.sqrt(d)) * math.log2(math.e)
+    g = torch.Generator("cpu").manual_seed(970 + d)
+    ramp = torch.linspace(0.0, 400.0 / (c * d), N)[None, None, :, None]
+    q = torch.ones((B, H, N, d)).to(torch.bfloat16)
+    k = (ramp + 0.05 * torch.randn((B, H, N, d), generator=g)).to(torch.bfloat16)
+    v = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    say(f"dropout rising scores d={d} causal={causal}")
+    o, l, _ = fa.forward_dropout(q.cuda(), k.cuda(), v.cuda(), p, seed, 0, causal=causal)
+    torch.cuda.synchronize()
+    q64, k64, v64 = (x.to(torch.float64).numpy() for x in (q, k, v))
+    oref, lref = Dr.dropout_forward_bhnd(q64, k64, v64, 1 / math.sqrt(d), causal, p, seed, 0)
+    me, re_ = errs(o.cpu().numpy(), oref)
+    le, _ = errs(l.cpu().numpy(), lref)
+    say(f"  O max-abs {me:.3e} rel-L2 {re_:.3e}  L max-abs {le:.3e}")
+    assert me <= O_MAX and re_ <= O_REL and le <= L_MAX
+
+
 def test_dropout_zero_probability_is_the_plain_path():
     t = inputs(1, 2, 300, 128, 961)
     q, k, v, do = gpu(t, "q", "k", "v", "do")

@@ -375,22 +375,20 @@ def test_fwd_late_max_rescale():
     check_fwd(o, l, oref, lref, "late max")
 
 
-def _rising_scores(B, H, N, gap_log2, seed, v_scale=1.0):
-    """Head width 128: every query is all ones and key j is t_j (1, ..., 1)
-    plus noise, with t_j rising along the keys so that the last key's score
-    is about gap_log2 (base-2 units of the scaled score) above the first's.
-    Each row's weights then grow along the keys, far past any reference taken
-    from the first keys."""
-    d = 128
-    t = shape_inputs(B, H, N, d, "bf16", seed)
+def _rising_scores(B, H, N, gap_log2, seed, v_scale=1.0, d=128, dv=None):
+    """Every query is all ones and key j is t_j (1, ..., 1) plus noise, with
+    t_j rising along the keys so that the last key's score is about gap_log2
+    (base-2 units of the scaled score) above the first's.  Each row's weights
+    then grow along the keys, far past any reference taken from the first
+    keys.  Head width d, value width dv (default d)."""
+    dv = d if dv is None else dv
     g = torch.Generator().manual_seed(seed)
     c = (1 / math.sqrt(d)) * math.log2(math.e)
     top = gap_log2 / (c * d)
     ramp = torch.linspace(0.0, top, N)[None, None, :, None]
-    t["q"] = torch.ones(B, H, N, d).to(torch.bfloat16)
-    t["k"] = (ramp + 0.05 * torch.randn(B, H, N, d, generator=g)).to(torch.bfloat16)
-    t["v"] = (v_scale * torch.randn(B, H, N, d, generator=g)).to(torch.bfloat16)
-    return t
+    return {"q": torch.ones(B, H, N, d).to(torch.bfloat16),
+            "k": (ramp + 0.05 * torch.randn(B, H, N, d, generator=g)).to(torch.bfloat16),
+            "v": (v_scale * torch.randn(B, H, N, dv, generator=g)).to(torch.bfloat16)}
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -448,6 +446,60 @@ def test_fwd_d128_rising_scores_general_and_strided(causal):
     views = [qkv[:, :, j].permute(0, 2, 1, 3).contiguous().to(torch.float64).numpy() for j in range(3)]
     oref, lref = oracle.attention_forward_bhnd(*views, 1 / math.sqrt(d), causal)
     check_fwd(o_s.cpu().numpy(), l_s.cpu().numpy(), oref, lref, f"rising strided causal={causal}")
+
+
+# The 32-row kernel (d = 64, dv != d, dropout, key ranges) takes each row's
+# reference from the first key tile its wave computes and restarts against
+# the exact max when a weight, a sum or an O element leaves float32.  Rising
+# scores drive rows past any early reference: gaps 60 and 110 stay finite,
+# 400 overflows and restarts.
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(1, 2, 2048), (1, 64, 1024)])
+@pytest.mark.parametrize("gap", [60.0, 110.0, 400.0])
+def test_fwd_d64_scores_rising_along_keys(B, H, N, gap, causal):
+    """(1, 2, 2048) runs the two-range launch, (1, 64, 1024) the 4-wave one."""
+    say(f"fwd d64 rising gap={gap} B={B} H={H} N={N} causal={causal}")
+    t = _rising_scores(B, H, N, gap, 320, d=64)
+    o, l = run_fwd(t, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(64))
+    check_fwd(o, l, oref, lref, f"d64 rising gap={gap} B={B} H={H} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_d64_large_values_with_rising_scores(causal):
+    """Values near 2^40 with weights up to about 2^100 over the first tile:
+    O leaves float32 unless the reference is the row max (restart)."""
+    B, H, N, vs = 1, 4, 1536, 2.0 ** 40
+    say(f"fwd d64 large values causal={causal}")
+    t = _rising_scores(B, H, N, 100.0, 321, v_scale=vs, d=64)
+    o, l = run_fwd(t, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(64))
+    check_fwd(o / vs, l, oref / vs, lref, f"d64 large values causal={causal}")
+
+
+@pytest.mark.parametrize("gap", [110.0, 400.0])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,dv", [(64, 128), (128, 64)])
+def test_fwd_rising_scores_mixed_widths(d, dv, causal, gap):
+    say(f"fwd rising d={d} dv={dv} gap={gap} causal={causal}")
+    t = _rising_scores(1, 3, 1100, gap, 322, d=d, dv=dv)
+    o, l = run_fwd(t, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(d))
+    check_fwd(o, l, oref, lref, f"rising d={d} dv={dv} gap={gap} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_splitkv_rising_scores(d, causal):
+    """Key ranges across workgroups: each range keeps its own reference and
+    restart; the merge of the ranges is the oracle's result."""
+    say(f"fwd splitkv rising d={d} causal={causal}")
+    t = _rising_scores(1, 2, 1500, 400.0, 323, d=d)
+    q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
+    o, l = fa.forward_splitkv(q, k, v, causal=causal, n_splits=4)
+    torch.cuda.synchronize()
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(d))
+    check_fwd(o.cpu().numpy(), l.cpu().numpy(), oref, lref, f"splitkv rising d={d} causal={causal}")
 
 
 def test_fwd_kv_permutation_invariance():

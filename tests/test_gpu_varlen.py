@@ -83,21 +83,22 @@ def test_varlen_forward_and_backward(li, causal, d):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen_d128_scores_rising_along_keys(causal):
-    """Head width 128, every query all ones and each sequence's keys rising
-    by about 400 base-2 units from its first key to its last: weights far
-    past float32 range against a reference taken from the first keys, in
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_scores_rising_along_keys(causal, d):
+    """Head widths 64 and 128, every query all ones and each sequence's keys
+    rising by about 400 base-2 units from its first key to its last: weights
+    far past float32 range against a reference taken from the first keys, in
     every sequence of the packed batch.  O, L, dK and dV match the oracle.
 
     dQ is only required to be finite here: it is sum_j dS_ij K_j with keys
-    that share a large common offset (about 24 per element), which cancels
+    that share a large common offset (24-35 per element), which cancels
     exactly only for exact dS.  The kernels round dS to bf16 for the matrix
     cores, and that rounding alone -- everything else in float64 -- already
     leaves dQ with a relative L2 error of 0.26-0.42 on these inputs.  The
     max-abs gates assume gradients of order one; here dK and dV reach about
     9 and 25, so their max-abs is gated relative to their largest value."""
-    lengths, H, d = [700, 0, 1500, 33], 2, 128
-    (q, k, v, do), cu = packed(lengths, H, d, 5200)
+    lengths, H = [700, 0, 1500, 33], 2
+    (q, k, v, do), cu = packed(lengths, H, d, 5200 + d)
     c = (1 / math.sqrt(d)) * math.log2(math.e)
     g = torch.Generator("cpu").manual_seed(5201)
     kf = torch.empty((H, int(cu[-1]), d))
@@ -107,7 +108,7 @@ def test_varlen_d128_scores_rising_along_keys(causal):
             kf[:, cu[b]:cu[b + 1]] = ramp + 0.05 * torch.randn((H, n, d), generator=g)
     q = torch.ones((H, int(cu[-1]), d)).to(torch.bfloat16)
     k = kf.to(torch.bfloat16)
-    say(f"varlen rising scores lengths={lengths} causal={causal}")
+    say(f"varlen rising scores lengths={lengths} d={d} causal={causal}")
     qg, kg, vg, dog = (x.cuda() for x in (q, k, v, do))
     cug = torch.from_numpy(cu).cuda()
     o, l = fa.forward_varlen(qg, kg, vg, cug, max(lengths), causal=causal)
