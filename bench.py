@@ -432,8 +432,8 @@ def main():
                  + bh * dc["Nq"] * (dc["dv"] + 1) * 4)
     dec_gbs = dec_bytes / (ms_dec * 1e-3) / 1e9
     # measured HBM bytes of the call: the key-range kernel and the merge
-    t_dec, dec_src = committed_traffic("decode_d128_rows1")
-    t_mrg, _ = committed_traffic("splitkv_merge_dv128")
+    t_dec, dec_src = committed_traffic("decode")
+    t_mrg, _ = committed_traffic("decode_merge")
     dec_traffic = t_dec + t_mrg if t_dec is not None and t_mrg is not None else None
 
     # ------------------------------------------------------------ the step with dropout
