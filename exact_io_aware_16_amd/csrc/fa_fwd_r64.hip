@@ -78,8 +78,9 @@ constexpr int kComputeUnits = 256;
 template <int SPLIT>
 struct Smem {
   bf16_raw k[SPLIT][kKSlots][kBC * kD];
-  // V ring: three slots with one key range (slots known at compile time in
-  // the three-tile loop), two with two ranges (LDS holds no more)
+  // V ring: three slots with one key range, two with two ranges (LDS holds
+  // no more); the steady loop unrolls over a multiple of both ring sizes so
+  // every slot is known at compile time
   static constexpr int kVSlots = SPLIT == 1 ? 3 : 2;
   bf16_raw v[SPLIT][kVSlots][kBC * kDV];
 };
@@ -493,14 +494,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_r64_kernel(
     };
     auto fast_step = [&](auto P, int v) { fast_step_at(P, ksub_addr(v + 1), vsub_addr(v), ksub_addr(v + 2)); };
     int u = 0;
-    if constexpr (SPLIT == 1) {
-      // Three LDS tiles per iteration from u = 0: tile u + i sits in slot i
-      // of both rings, so every operand address is a lane register plus an
+    {
+      // TPI LDS tiles per iteration from u = 0, a multiple of both ring
+      // sizes: tile u + i sits in slot i % 3 of the K ring and i % kVSlots of
+      // the V ring, so every operand address is a lane register plus an
       // immediate offset (no address arithmetic in the loop).
-      constexpr auto koff = [](int j) { return (uint32_t)(((j >> 1) % 3) * (int)kTileBytes + (j & 1) * (int)kSubBytes); };
-      constexpr auto voff = [](int j) { return (uint32_t)(((j >> 1) % 3) * (int)vTileBytes + (j & 1) * (int)kSubBytes); };
-      for (; 2 * u + 6 < n_clean; u += 3) {
-        static_for<0, 3>([&](auto I) {
+      constexpr int TPI = kVSlots == kKSlots ? kKSlots : kKSlots * kVSlots;
+      constexpr auto koff = [](int j) {
+        return (uint32_t)(((j >> 1) % kKSlots) * (int)kTileBytes + (j & 1) * (int)kSubBytes);
+      };
+      constexpr auto voff = [](int j) {
+        return (uint32_t)(((j >> 1) % kVSlots) * (int)vTileBytes + (j & 1) * (int)kSubBytes);
+      };
+      for (; 2 * u + 2 * TPI < n_clean; u += TPI) {
+        static_for<0, TPI>([&](auto I) {
           constexpr int i = decltype(I)::value;
           top(u + i);
           fast_step_at(ic<0>{}, koff(2 * i + 1), voff(2 * i), koff(2 * i + 2));
