@@ -151,6 +151,31 @@ def test_dropout_forward_rising_scores(d, causal):
     assert me <= O_MAX and re_ <= O_REL and le <= L_MAX
 
 
+def test_dropout_forward_rising_scores_large_grid():
+    """The same restart in the 4-wave launch (512 workgroups, two per CU):
+    d = 64, 64 heads with keys rising by about 400 base-2 units; a sample of
+    heads against the dropout oracle."""
+    B, H, N, d, p, seed = 1, 64, 1024, 64, 0.3, 4343
+    c = (1 / math.sqrt(d)) * math.log2(math.e)
+    g = torch.Generator("cpu").manual_seed(975)
+    ramp = torch.linspace(0.0, 400.0 / (c * d), N)[None, None, :, None]
+    q = torch.ones((B, H, N, d)).to(torch.bfloat16)
+    k = (ramp + 0.05 * torch.randn((B, H, N, d), generator=g)).to(torch.bfloat16)
+    v = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    say("dropout rising scores, large grid, d=64 causal")
+    o, l, _ = fa.forward_dropout(q.cuda(), k.cuda(), v.cuda(), p, seed, 0, causal=True)
+    torch.cuda.synchronize()
+    t_ = Dr.keep_threshold(p)
+    for h in (0, 21, 63):
+        q64, k64, v64 = (x[0, h].to(torch.float64).numpy() for x in (q, k, v))
+        keep = Dr.dropout_keep(np.arange(N), N, h, seed, 0, t_)
+        oref, lref = Dr.attention_forward_dropout(q64, k64, v64, 1 / math.sqrt(d), True, keep, t_)
+        me, re_ = errs(o[0, h].cpu().numpy(), oref)
+        le, _ = errs(l[0, h].cpu().numpy(), lref)
+        say(f"  head {h}: O max-abs {me:.3e} rel-L2 {re_:.3e}  L max-abs {le:.3e}")
+        assert me <= O_MAX and re_ <= O_REL and le <= L_MAX, h
+
+
 def test_dropout_zero_probability_is_the_plain_path():
     t = inputs(1, 2, 300, 128, 961)
     q, k, v, do = gpu(t, "q", "k", "v", "do")
