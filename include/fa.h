@@ -71,10 +71,12 @@ typedef enum {
  *             choice; the caller may pass another).  0 weighs every visible
  *             key equally (O = their mean, L = ln of their count); a negative
  *             scale reverses the order of the scores.
- * Scores and their running max/sum stay on chip: S = Q K^T is formed one
- * key tile at a time on bf16 matrix cores with float32 accumulation, the
- * probabilities are rounded to bf16 for the P V product, and O is divided by
- * the running sum once, after the last tile.
+ * Scores and the row sums stay on chip: S = Q K^T is formed one key tile at
+ * a time on bf16 matrix cores with float32 accumulation; the weights are
+ * taken against a per-row reference (the exact max of the row's first keys,
+ * or of all its keys if float32 would overflow otherwise, "What it doesn't
+ * solve" on the first page), rounded to bf16 for the P V product, and O is
+ * divided by the row sum once, after the last tile.
  */
 int fa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
