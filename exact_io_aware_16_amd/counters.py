@@ -320,8 +320,47 @@ def markdown_counters(rec, args):
                 "core was busy; SQ_WAIT_ANY / SQ_WAVE_CYCLES (both in quad-cycles) is the share of wave time",
                 "spent waiting on dependencies; SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE is the fraction of",
                 "LDS cycles lost to conflicts."]
+        out += markdown_shares(rec)
     out.append("")
     return "\n".join(out)
+
+
+NOMINAL_CLOCK_HZ = 2.4e9
+SIMDS = 1024  # 256 compute units x 4
+
+
+def markdown_shares(rec):
+    """Shares derived from the SQ sums and each launch's average duration in
+    the kernel trace of the bench run."""
+    stats = rec.get("kernel_stats") or {}
+    rows = []
+    for k in COUNTED:
+        d, kern = rec["sq"].get(k), rec["kernels"].get(k)
+        st = stats.get(kern["launch"]) if kern else None
+        if not (d and st):
+            continue
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        n_mfma = busy / 32.0
+        simd_cycles = st["avg_ns"] * 1e-9 * NOMINAL_CLOCK_HZ * SIMDS
+        pct = lambda a, b: f"{100.0 * a / b:.1f}%" if b else "—"
+        rows.append(f"| {k} | {st['avg_ns'] / 1e3:.1f} | {pct(busy, simd_cycles) if busy else '—'} | "
+                    f"{d.get('SQ_INSTS_VALU', 0.0) / n_mfma:.2f} | " if n_mfma else
+                    f"| {k} | {st['avg_ns'] / 1e3:.1f} | — | — | ")
+        rows[-1] += (f"{pct(d.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0.0), busy) if busy else '—'} | "
+                     f"{pct(d.get('SQ_WAIT_ANY', 0.0), d.get('SQ_WAVE_CYCLES', 0.0))} | "
+                     f"{pct(d.get('SQ_LDS_BANK_CONFLICT', 0.0), d.get('SQ_LDS_IDX_ACTIVE', 0.0))} |")
+    if not rows:
+        return []
+    return ["", "## Shares per launch", "",
+            "From the sums above and the launch's average duration in the kernel trace of the bench run",
+            "(`kernel_trace_bench_workloads.md`).  The matrix-core share divides the MFMA-busy cycles by",
+            "1024 SIMDs at the nominal 2.4 GHz; under load the chip runs slower (2.05-2.2 GHz on these",
+            "boxes), so the share at the real clock is that much higher.  Vector instructions are",
+            "SQ_INSTS_VALU per 32x32x16 MFMA (32 busy cycles each); the count includes the MFMAs",
+            "themselves (the 64-row forward's loop has 4.5 other vector instructions per MFMA).", "",
+            "| entry | avg µs | matrix core busy (2.4 GHz) | vector instr. per MFMA | MFMA-busy cycles with a vector issue | "
+            "wave cycles waiting | LDS cycles in bank conflicts |",
+            "|---|---|---|---|---|---|---|"] + rows
 
 
 def markdown_stats(stats, args):
