@@ -491,6 +491,26 @@ def test_fwd_rising_scores_mixed_widths(d, dv, causal, gap):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
+def test_fwd_overflow_in_one_key_range_only(d, causal):
+    """Keys flat over the first half of the sequence and rising by about 400
+    base-2 units over the second: in the two-range launch (B1 H2 N2048) only
+    the workgroup's second key range overflows, and the whole workgroup must
+    run again against the exact max (both ranges feed one merge)."""
+    B, H, N = 1, 2, 2048
+    say(f"fwd overflow in one key range d={d} causal={causal}")
+    g = torch.Generator().manual_seed(324)
+    c = (1 / math.sqrt(d)) * math.log2(math.e)
+    ramp = torch.cat([torch.zeros(N // 2), torch.linspace(0.0, 400.0 / (c * d), N // 2)])[None, None, :, None]
+    t = {"q": torch.ones(B, H, N, d).to(torch.bfloat16),
+         "k": (ramp + 0.05 * torch.randn(B, H, N, d, generator=g)).to(torch.bfloat16),
+         "v": torch.randn(B, H, N, d, generator=g).to(torch.bfloat16)}
+    o, l = run_fwd(t, causal)
+    oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(d))
+    check_fwd(o, l, oref, lref, f"overflow in one key range d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
 def test_fwd_splitkv_rising_scores(d, causal):
     """Key ranges across workgroups: each range keeps its own reference and
     restart; the merge of the ranges is the oracle's result."""
