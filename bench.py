@@ -27,8 +27,10 @@ Also reported on the same line:
              d=128; fa_fwd_varlen + fa_bwd_varlen) against the same batch
              padded to the longest sequence in the dense layout
   phases     forward and backward of the step timed separately
-  kernels    each kernel of the step timed alone through its C entry point
-             (fa_fwd, fa_bwd_prep, fa_bwd_dkdv, fa_bwd_dq)
+  kernels    the forward and the three backward phases, each timed alone
+             through its C entry point (fa_fwd, fa_bwd_prep, fa_bwd_dkdv,
+             fa_bwd_dq); fa_bwd itself runs the dQ pass with the preprocess
+             fused in, then dK/dV (that dQ launch is in the kernel trace)
   roofline   the dominant kernel of the step against the bf16 matrix-core
              peak; traffic from committed rocprofv3 counters when they were
              taken on the current kernel sources
@@ -287,7 +289,8 @@ def main():
     # that neither the parts nor the step below are timed during the ramp
     steady(step, 1.0)
 
-    # each kernel of the step alone (workspace prepared once for the two passes)
+    # the forward and each backward phase alone (workspace prepared once for
+    # the two passes); fa_bwd runs dQ with the preprocess fused in, then dK/dV
     dq_o, dk_o, dv_o = (torch.empty_like(o) for _ in range(3))
     fa.backward_prep(o, lse, do, ws)
     torch.cuda.synchronize()

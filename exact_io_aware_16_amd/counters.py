@@ -68,11 +68,14 @@ def kernel_key(name):
     if m:
         return f"splitkv_merge_dv{m.group(1)}"
     for kern, short in (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq")):
-        m = re.search(kern + r"(?:ILi|<)(\d+)(?:ELb|, )" + b + r"(?:(?:ELb|, )" + b + r")?", name)
+        m = re.search(kern + r"(?:ILi|<)(\d+)(?:ELb|, )" + b + r"(?:(?:ELb|, )" + b + r")?(?:(?:ELb|, )" + b + r")?",
+                      name)
         if m:
             causal = m.group(2) in ("1", "true")
             drop = m.group(3) in ("1", "true")
-            return f"{short}_d{m.group(1)}" + ("_causal" if causal else "") + ("_dropout" if drop else "")
+            fused = m.group(4) in ("1", "true")  # the dQ pass with the preprocess fused in (fa_bwd)
+            return (f"{short}{'_fused' if fused else ''}_d{m.group(1)}" + ("_causal" if causal else "")
+                    + ("_dropout" if drop else ""))
     m = re.search(r"bwd_pre_kernel(?:ILi|<)(\d+)", name)
     if m:
         return f"bwd_pre_d{m.group(1)}"
@@ -107,8 +110,14 @@ def run():
             o, lse = fa.forward(q, k, v, causal=w.causal)
         if w.backward:
             do = t["do"].to(dev)
+            # fa_bwd (dQ with the preprocess fused in, then dK/dV) and the
+            # separate phases (preprocess, dK/dV, dQ)
             for _ in range(REPEAT):
                 fa.backward(q, k, v, o, lse, do, causal=w.causal)
+            for _ in range(REPEAT):
+                ws = fa.backward_prep(o, lse, do, None)
+                fa.backward_dkdv(q, k, v, do, ws, causal=w.causal)
+                fa.backward_dq(q, k, v, do, ws, causal=w.causal)
         torch.cuda.synchronize()
         del q, k, v, o, lse
         print(f"ran {w.name}", flush=True)
@@ -259,6 +268,11 @@ COUNTED = {
     # S and dP are computed a second time (1.5x the forward executed)
     "bwd_dq": ("bwd_dq_d128_causal", 32 * 32, "B=2 H=16 N=4096 d=128 causal",
                4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 8 + 32 * 4096 * 128 * 4, 0.5 * _F5, 1.5 * _F5),
+    # fa_bwd's dQ pass: as bwd_dq, plus O and L read to compute the two
+    # workspace floats per row itself (written, not read)
+    "bwd_dq_fused": ("bwd_dq_fused_d128_causal", 32 * 32, "B=2 H=16 N=4096 d=128 causal",
+                     4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 128 * 4 + 32 * 4096 * 4 + 32 * 4096 * 8
+                     + 32 * 4096 * 128 * 4, 0.5 * _F5, 1.5 * _F5),
     # decode, 16 key ranges: reads Q, K, V once, writes 16 partial (O, L) per row
     "decode": ("decode_d128_rows1", 32 * 16, "decode B=1 H=32 Nq=1 Nk=32768 d=128",
                32 * 128 * 2 + 2 * 32 * 32768 * 128 * 2 + 16 * 32 * 129 * 4, 0.0, 0.0),

@@ -659,13 +659,13 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const fl
                            float scale, int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
   const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
   const long long rows = workspace_rows(BH, N, sq);
-  // the preprocess is row-wise: all H * total packed rows at once
-  hipError_t e = sq.cu ? launch_bwd_prep(dout, o, lse, ws, sq.H, sq.total, d, scale, stream)
-                       : launch_bwd_prep(dout, o, lse, ws, BH, N, d, scale, stream);
+  // The dQ pass computes the row statistics of its own rows (the
+  // preprocess, fused: every row belongs to exactly one of its workgroups)
+  // and stores them for the dK/dV pass, which runs after it on the stream.
+  hipError_t e = launch_bwd_dq_fused(q, k, v, dout, o, lse, ws + rows, ws, dq, BH, N, d, scale, causal, drop, seqs,
+                                     stream);
   if (e != hipSuccess) return e;
-  e = launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, N, d, scale, causal, drop, seqs, stream);
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, BH, N, d, scale, causal, drop, seqs, stream);
+  return launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, N, d, scale, causal, drop, seqs, stream);
 }
 
 }  // namespace fa

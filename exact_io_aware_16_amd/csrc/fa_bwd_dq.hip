@@ -76,11 +76,16 @@ struct KvCopy {
   }
 };
 
-template <int D, bool CAUSAL, bool DROP>
+// FUSED: the row statistics the backward needs (scale D = scale dO . O and
+// L log2(e)) are computed here from O and L for this workgroup's rows and
+// stored to L2 / Dsc for the dK/dV pass, which then runs after this one;
+// otherwise they are read from L2 / Dsc (written by bwd_pre_kernel).
+template <int D, bool CAUSAL, bool DROP, bool FUSED>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
-    const bf16_raw* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dsc,
-    float* __restrict__ dQ, int N, int n_qblk, int total, float scale, float c, Dropout drop, Seqs seqs) {
+    const bf16_raw* __restrict__ dO, float* __restrict__ L2, float* __restrict__ Dsc, const float* __restrict__ O,
+    const float* __restrict__ LSE, float* __restrict__ dQ, int N, int n_qblk, int total, float scale, float c,
+    Dropout drop, Seqs seqs) {
   constexpr int BC = DqTile<D>::BC;
   constexpr int NKB = BC / 32;  // 32-key blocks per tile
   constexpr int NKK = D / 16;   // 16-wide head-dim slices (contraction of S and dP)
@@ -162,14 +167,55 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
       qf[kk] = as_bf16x8(ld16(Qrow + 16 * kk + 8 * g));
       dof[kk] = as_bf16x8(ld16(Grow + 16 * kk + 8 * g));
     }
+    // fused: this row's O (elements 16 kk + 8 g .. + 7) and L, in flight
+    // with Q and dO
+    float4 orow[FUSED ? 2 * NKK : 1];
+    float lse_q = 0.f;
+    if constexpr (FUSED) {
+      lse_q = LSE[row0 + qr];
+      const float* Orow = O + (row0 + qr) * D;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        orow[2 * kk] = *reinterpret_cast<const float4*>(Orow + 16 * kk + 8 * g);
+        orow[2 * kk + 1] = *reinterpret_cast<const float4*>(Orow + 16 * kk + 8 * g + 4);
+      }
+    }
     // in AGPRs for the whole kernel: they leave the VGPRs to the products
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       asm volatile("" : "+a"(qf[kk]));
       asm volatile("" : "+a"(dof[kk]));
     }
-    l2q = L2[row0 + qr];
-    dq_sc = Dsc[row0 + qr];
+    if constexpr (FUSED) {
+      // D = dO . O of this row, summed in the order of bwd_pre_kernel (so the
+      // statistics, and every gradient, are bitwise those of the separate
+      // preprocess): part p = 2 kk + g holds elements 8p .. 8p+7, each part a
+      // chain of fused multiply-adds, the parts combined as p ^ 8, p ^ 4,
+      // p ^ 2 (in this lane) and p ^ 1 (the lane of the other half).
+      float part[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const float4 o0 = orow[2 * kk], o1 = orow[2 * kk + 1];
+        const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)dof[kk][e], ov[e], acc);
+        part[kk] = acc;
+      }
+#pragma unroll
+      for (int sft = NKK / 2; sft > 0; sft >>= 1)
+#pragma unroll
+        for (int kk = 0; kk < sft; ++kk) part[kk] = part[kk] + part[kk + sft];
+      dq_sc = scale * halves_sum(part[0]);
+      l2q = lse_q * kLog2e;
+      if (g == 0 && my_q < N) {
+        Dsc[row0 + my_q] = dq_sc;
+        L2[row0 + my_q] = l2q;
+      }
+    } else {
+      l2q = L2[row0 + qr];
+      dq_sc = Dsc[row0 + qr];
+    }
   }
 
   f32x16 dq_acc[NDB];
@@ -489,29 +535,49 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   }
 }
 
+// o, lse non-null: the fused launch (statistics computed here and stored to
+// l2 / dsc); else l2 / dsc hold them already
 template <int D, bool CAUSAL, bool DROP>
-hipError_t launch(const void* q, const void* k, const void* v, const void* dout, const float* l2, const float* dsc,
-                  float* dq, int BH, int N, float scale, const Dropout& drop, const Seqs& sq, hipStream_t stream) {
+hipError_t launch(const void* q, const void* k, const void* v, const void* dout, float* l2, float* dsc,
+                  const float* o, const float* lse, float* dq, int BH, int N, float scale, const Dropout& drop,
+                  const Seqs& sq, hipStream_t stream) {
   const int n_qblk = (N + kBR - 1) / kBR;
   const long long total = (long long)BH * n_qblk;
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP>), dim3(grid), dim3(kThreads), 0, stream,
-                     static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k), static_cast<const bf16_raw*>(v),
-                     static_cast<const bf16_raw*>(dout), l2, dsc, dq, N, n_qblk, (int)total, scale, scale * kLog2e,
-                     drop, sq);
+  if (o)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP, true>), dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
+                       static_cast<const bf16_raw*>(v), static_cast<const bf16_raw*>(dout), l2, dsc, o, lse, dq, N,
+                       n_qblk, (int)total, scale, scale * kLog2e, drop, sq);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
+                       static_cast<const bf16_raw*>(v), static_cast<const bf16_raw*>(dout), l2, dsc, o, lse, dq, N,
+                       n_qblk, (int)total, scale, scale * kLog2e, drop, sq);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_drop(const void* q, const void* k, const void* v, const void* dout, const float* l2,
-                       const float* dsc, float* dq, int BH, int N, float scale, const Dropout* drop, const Seqs& sq,
-                       hipStream_t stream) {
+hipError_t launch_drop(const void* q, const void* k, const void* v, const void* dout, float* l2, float* dsc,
+                       const float* o, const float* lse, float* dq, int BH, int N, float scale, const Dropout* drop,
+                       const Seqs& sq, hipStream_t stream) {
   if (drop) {
     if (sq.cu) return hipErrorInvalidValue;  // dropout is offered for the dense layout only
-    return launch<D, CAUSAL, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, *drop, sq, stream);
+    return launch<D, CAUSAL, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, *drop, sq, stream);
   }
-  return launch<D, CAUSAL, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, Dropout{}, sq, stream);
+  return launch<D, CAUSAL, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, Dropout{}, sq, stream);
+}
+
+hipError_t launch_any(const void* q, const void* k, const void* v, const void* dout, float* l2, float* dsc,
+                      const float* o, const float* lse, float* dq, int BH, int N, int d, float scale, int causal,
+                      const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+  const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
+  if (d == 128)
+    return causal ? launch_drop<128, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, drop, sq, stream)
+                  : launch_drop<128, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, drop, sq, stream);
+  return causal ? launch_drop<64, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, drop, sq, stream)
+                : launch_drop<64, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, drop, sq, stream);
 }
 
 }  // namespace
@@ -519,11 +585,15 @@ hipError_t launch_drop(const void* q, const void* k, const void* v, const void* 
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
                               const float* dsc, float* dq, int BH, int N, int d, float scale, int causal,
                               const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
-  const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
-  if (d == 128) return causal ? launch_drop<128, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, sq, stream)
-                              : launch_drop<128, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, sq, stream);
-  return causal ? launch_drop<64, true>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, sq, stream)
-                : launch_drop<64, false>(q, k, v, dout, l2, dsc, dq, BH, N, scale, drop, sq, stream);
+  // statistics only read on this launch
+  return launch_any(q, k, v, dout, const_cast<float*>(l2), const_cast<float*>(dsc), nullptr, nullptr, dq, BH, N, d,
+                    scale, causal, drop, seqs, stream);
+}
+
+hipError_t launch_bwd_dq_fused(const void* q, const void* k, const void* v, const void* dout, const float* o,
+                               const float* lse, float* l2, float* dsc, float* dq, int BH, int N, int d, float scale,
+                               int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+  return launch_any(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, d, scale, causal, drop, seqs, stream);
 }
 
 }  // namespace fa

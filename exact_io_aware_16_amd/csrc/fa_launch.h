@@ -61,6 +61,12 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
                               const float* dsc, float* dq, int BH, int N, int d, float scale, int causal,
                               const Dropout* drop, const Seqs* seqs, hipStream_t stream);
+// The dQ pass with the preprocess fused in: computes scale D = scale dO . O and
+// L log2(e) of its rows from o and lse (bitwise as launch_bwd_prep does),
+// stores them to l2 / dsc for a dK/dV launch that follows, and writes dq.
+hipError_t launch_bwd_dq_fused(const void* q, const void* k, const void* v, const void* dout, const float* o,
+                               const float* lse, float* l2, float* dsc, float* dq, int BH, int N, int d, float scale,
+                               int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream);
 
 // Backward phases (fa_bwd.hip); ws holds [scale * D | L log2(e)], BH * N
 // floats each.

@@ -161,11 +161,11 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   workspace     : device, >= fa_bwd_workspace_bytes(B,H,N,d) bytes; its
  *                   contents on entry do not matter
  * The probability tiles are rebuilt from Q, K and lse; no N x N tensor is
- * stored.  Three kernels run on `stream`: a per-row preprocess, a
- * key-stationary pass for dk and dv, and a query-stationary pass for dq
+ * stored.  Two kernels run on `stream`: a query-stationary pass for dq
  * (which recomputes the score tiles instead of summing partial dq with
- * atomics).  Every output element is written once: results are
- * deterministic.
+ * atomics, and first computes the per-row statistics the backward needs,
+ * storing them to the workspace), then a key-stationary pass for dk and dv.
+ * Every output element is written once: results are deterministic.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
            const void* dout, float* dq, float* dk, float* dv, void* workspace,
@@ -252,11 +252,12 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const float* o, c
                   float scale, int causal, hipStream_t stream);
 
 /*
- * The three phases fa_bwd runs, for callers that schedule or time them
+ * The backward in three phases, for callers that schedule or time them
  * separately (same arguments, layouts and errors as fa_bwd; workspace as
- * sized by fa_bwd_workspace_bytes).  fa_bwd(...) is exactly
+ * sized by fa_bwd_workspace_bytes).  On one stream
  *   fa_bwd_prep(...); fa_bwd_dkdv(...); fa_bwd_dq(...);
- * on one stream, and the results are bitwise the same.
+ * gives bitwise the results of fa_bwd, which runs the preprocess inside its
+ * dQ pass (same summation order) and the dK/dV pass after it.
  *
  * fa_bwd_prep: per query row, scale * (dO_i . O_i) and L_i log2(e) into the
  *   workspace.  Reads dout, o, lse.

@@ -639,16 +639,21 @@ def test_bwd_ragged(N, d, causal):
 
 @pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
 def test_bwd_phases_compose_to_fa_bwd(d, causal):
-    # fa_bwd is fa_bwd_prep; fa_bwd_dkdv; fa_bwd_dq on one stream: bitwise equal
+    # fa_bwd runs the dQ pass with the preprocess fused in, then dK/dV; the
+    # phases run fa_bwd_prep; fa_bwd_dkdv; fa_bwd_dq.  The row statistics in
+    # the workspace and every gradient are bitwise equal.
     t = shape_inputs(1, 2, 300, d, "bf16", 500 + d, with_do=True)
     q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
     say(f"bwd phases d={d} causal={causal}")
     o, l = fa.forward(q, k, v, causal=causal)
-    dq, dk, dv = fa.backward(q, k, v, o, l, do, causal=causal)
+    ws1 = fa.backward_prep(o, l, do, None).fill_(0xAB)
+    dq, dk, dv = fa.backward(q, k, v, o, l, do, causal=causal, workspace=ws1)
     ws = fa.backward_prep(o, l, do, None)
     dk2, dv2 = fa.backward_dkdv(q, k, v, do, ws, causal=causal)
     dq2 = fa.backward_dq(q, k, v, do, ws, causal=causal)
     torch.cuda.synchronize()
+    rows = 2 * 300
+    assert torch.equal(ws1[:8 * rows], ws[:8 * rows])  # scale D and L log2(e), float32 each
     for a_, b_ in ((dq, dq2), (dk, dk2), (dv, dv2)):
         assert torch.equal(a_, b_)
 
