@@ -191,10 +191,18 @@ struct Wave {
   // is computed: nothing in the loop reads it before commit(), and the
   // compiler otherwise sinks every piece's add past the loop's tile branches
   // into one burst of vector work with no product beside it.
-  __device__ __forceinline__ void piece(int p, int h, int q) {
+  // MASKED: keys past the row's last visible key get weight 0; lim is that
+  // key minus (first key of the sub-tile + 8 g), so register 8 kg + e (key
+  // 16 kg + 8 g + e of the sub-tile) is visible iff 16 kg + e <= lim.
+  template <bool MASKED = false>
+  __device__ __forceinline__ void piece(int p, int h, int q, int lim = 0) {
     const int kg = q >> 2, e0 = 2 * (q & 3);
 #pragma unroll
-    for (int e = e0; e < e0 + 2; ++e) pf[h][kg][e] = fast_exp2(fmaf(s[p][h][8 * kg + e], c, -hs[h].m_use));
+    for (int e = e0; e < e0 + 2; ++e) {
+      float x = s[p][h][8 * kg + e];
+      if constexpr (MASKED) x = 16 * kg + e > lim ? -INFINITY : x;
+      pf[h][kg][e] = fast_exp2(fmaf(x, c, -hs[h].m_use));
+    }
     part[h][q] = pf[h][kg][e0] + pf[h][kg][e0 + 1];
     asm volatile("" : "+v"(part[h][q]));
     if ((q & 3) == 3) pb[p][h][kg] = pack_bf16x8(pf[h][kg]);
@@ -241,8 +249,8 @@ struct Wave {
   // read; weight piece kk follows.  LOAD_V: the first two V^T operands of phase 2 load in the last
   // groups.  The product before the phase read av[1] and pb[pn][1][1] (the
   // last product of phase 2).
-  template <bool WITH_SOFT, bool LOAD_V>
-  __device__ __forceinline__ void phase1(int pc, int pn, uint32_t ksub, uint32_t vsub) {
+  template <bool WITH_SOFT, bool LOAD_V, bool MASKED = false>
+  __device__ __forceinline__ void phase1(int pc, int pn, uint32_t ksub, uint32_t vsub, int lim = 0) {
     static_for<0, kNKK>([&](auto KK) {
       constexpr int kk = decltype(KK)::value;
       s[pn][0] = mfma32(ak[kk % 3], qf[0][kk], kk == 0 ? f32x16{} : s[pn][0]);
@@ -252,7 +260,7 @@ struct Wave {
       if constexpr (LOAD_V && kk >= kNKK - 2) load_v(kk - (kNKK - 2), vsub);
       s[pn][1] = mfma32(ak[kk % 3], qf[1][kk], kk == 0 ? f32x16{} : s[pn][1]);
       anchor(s[pn][1]);
-      if constexpr (WITH_SOFT) piece(pc, 1, kk);
+      if constexpr (WITH_SOFT) piece<MASKED>(pc, 1, kk, lim);
       sg<kSgMfma, 1>(); sg<kSgDsRead, 2>(); sg<kSgValu, 4>(); sg<kSgMfma, 1>(); sg<kSgValu, 30>();
       group_fence();
     });
@@ -266,8 +274,8 @@ struct Wave {
   // next sub-tile is not read right after its last product).  NEXT_K:
   // slices 0 and 1 of the sub-tile after next load in the last groups.  The
   // product before the phase read ak[1] (and Q).
-  template <bool WITH_SOFT, bool NEXT_K>
-  __device__ __forceinline__ void phase2(int pc, int pn, uint32_t vsub, uint32_t knext) {
+  template <bool WITH_SOFT, bool NEXT_K, bool MASKED = false>
+  __device__ __forceinline__ void phase2(int pc, int pn, uint32_t vsub, uint32_t knext, int lim = 0) {
     static_for<0, 2 * kNDB>([&](auto GI) {
       constexpr int gi = decltype(GI)::value;
       constexpr int kg = gi / kNDB, db = gi % kNDB;
@@ -279,10 +287,10 @@ struct Wave {
       o[1][db] = mfma32(av[gi % 3], pb[pc][1][kg], o[1][db]);
       after(o[1][db], pb[pc][0][kg]);
       if constexpr (WITH_SOFT && gi == 1) {
-        piece(pn, 0, 0);
-        piece(pn, 0, 1);
+        piece<MASKED>(pn, 0, 0, lim);
+        piece<MASKED>(pn, 0, 1, lim);
       }
-      if constexpr (WITH_SOFT && gi >= 2) piece(pn, 0, gi);
+      if constexpr (WITH_SOFT && gi >= 2) piece<MASKED>(pn, 0, gi, lim);
       sg<kSgMfma, 1>(); sg<kSgDsRead, 2>(); sg<kSgValu, 4>(); sg<kSgMfma, 1>(); sg<kSgValu, 30>();
       group_fence();
     });
@@ -521,18 +529,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_r64_kernel(
       fast_step(ic<1>{}, 2 * u + 1);
     }
     // The last sub-tiles of the wave (masks; possibly no next sub-tile) and
-    // the iterations a wave only helps with copies.  Masks are selects (a
-    // clean sub-tile masks nothing); S of a missing next sub-tile is computed
-    // from a resident tile and its weights are never committed.
+    // the iterations a wave only helps with copies.  Masks are selects in the
+    // weight pieces, on the values as they leave the accumulators (a clean
+    // sub-tile masks nothing); S of a missing next sub-tile is computed from a
+    // resident tile and its weights are never committed.
     auto tail_step = [&](auto P, int v) {
       constexpr int pc = decltype(P)::value, pn = 1 - pc;
       const bool has_next = v + 1 < n_w;
       const int vn = has_next ? v + 1 : v;
-      w.apply_mask(pc, 1, key_a + v * kSub);
-      w.template phase1<true, true>(pc, pn, ksub_addr(vn), vsub_addr(v));
+      const int g8 = 8 * ((threadIdx.x >> 5) & 1);
+      w.template phase1<true, true, true>(pc, pn, ksub_addr(vn), vsub_addr(v), w.last_key[1] - (key_a + v * kSub + g8));
       w.commit(1);
-      w.apply_mask(pn, 0, key_a + vn * kSub);
-      w.template phase2<true, true>(pc, pn, vsub_addr(v), ksub_addr(has_next ? v + 2 : v));
+      w.template phase2<true, true, true>(pc, pn, vsub_addr(v), ksub_addr(has_next ? v + 2 : v),
+                                          w.last_key[0] - (key_a + vn * kSub + g8));
       if (has_next) w.commit(0);
     };
     for (; u < n_iter; ++u) {
