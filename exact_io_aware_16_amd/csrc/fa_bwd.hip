@@ -214,7 +214,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint32_t off = (uint32_t)(my_key * D + 16 * kk + 8 * g) * 2u;
     kres[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
     vres[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
-    // kept in AGPRs, which the matrix cores read directly
+  }
+  // kept in AGPRs, which the matrix cores read directly.  The pins follow
+  // all of the loads: a pin reads its register, so a pin right behind its
+  // load would wait for it, one memory round trip per slice.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
     asm volatile("" : "+a"(kres[kk]));
     asm volatile("" : "+a"(vres[kk]));
   }

@@ -401,12 +401,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_r64_kernel(
   // scale sign folded into Q (exact: a sign flip of bf16), c = |scale| log2 e
   w.c = fabsf(c_in);
   const uint32_t qsign = c_in < 0.f ? 0x80008000u : 0u;
+  // All of the wave's Q loads are issued before any is moved: a move right
+  // behind its load waits for it, and sixteen such waits in a row cost
+  // sixteen memory round trips before the first product.
+  uint4 xq[2][kNKK];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int qr = min(r0 + 32 * h + col, Nq - 1);
 #pragma unroll
+    for (int kk = 0; kk < kNKK; ++kk) xq[h][kk] = ld16(Qh + (size_t)qr * q_stride + 16 * kk + 8 * g);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
     for (int kk = 0; kk < kNKK; ++kk) {
-      uint4 x = ld16(Qh + (size_t)qr * q_stride + 16 * kk + 8 * g);
+      uint4 x = xq[h][kk];
       x.x ^= qsign; x.y ^= qsign; x.z ^= qsign; x.w ^= qsign;
       w.qf[h][kk] = as_bf16x8(x);
       // Q stays in AGPRs for the whole kernel (the matrix core reads its B
