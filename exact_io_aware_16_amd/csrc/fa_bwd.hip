@@ -13,17 +13,17 @@
 //   dS' = scale dS = P * (scale dP - scale D)
 // (scale D comes from the preprocess), so dK = dS'^T Q and dQ = dS' K.
 //
-// Kernels (three launches, no atomics, every output written once):
+// Kernels (no atomics, every output written once; fa_bwd launches the dQ
+// pass with the preprocess folded in, then dK/dV):
 //  * bwd_pre_kernel: per query row scale * (dO_i . O_i) and L_i log2(e) into
-//    the workspace.
+//    the workspace (the separate preprocess phase).
 //  * bwd_dkdv_kernel: one workgroup per (head, block of 128 keys).  Each of
-//    its 4 waves owns 32 keys: their V rows stay in registers (B operands of
-//    dP = dO V^T), their K rows come from the block's K tile in LDS (B
-//    operands of S = Q K^T), and dK^T, dV^T accumulate in registers.  The
-//    workgroup walks the query rows 64 at a time (causal: from the block's
-//    diagonal on).  Per step:
+//    its 4 waves owns 32 keys: their K and V rows stay in AGPRs for the whole
+//    kernel (B operands of S = Q K^T and dP = dO V^T), and dK^T, dV^T
+//    accumulate in registers.  The workgroup walks the query rows 64 at a
+//    time (causal: from the block's diagonal on).  Per step:
 //      A. S and dP for the 64 rows of the tile (Q and dO tiles arrive by
-//         LDS-direct buffer loads, double buffered, rows in perm32 order so
+//         LDS-direct buffer loads, three buffers, rows in perm32 order so
 //         that S and dP come out with 8 consecutive query rows per register
 //         octet -- the B-operand layout of dV^T = dO^T P and dK^T = Q^T dS');
 //      B. P and dS' on the vector ALUs;
@@ -32,7 +32,8 @@
 //    One barrier per step publishes the tile and frees the buffer the step
 //    refills.
 //  * bwd_dq_kernel (fa_bwd_dq.hip): query-stationary, recomputes S and dP
-//    per key tile and accumulates dQ in registers.
+//    per key tile and accumulates dQ in registers; in fa_bwd it also forms
+//    the row statistics of its rows for the dK/dV pass.
 // dQ is not accumulated across key blocks with atomics: on this part
 // device-scope float atomics are performed at the memory side, and the
 // partial sums of every key block would cross the fabric once each; the

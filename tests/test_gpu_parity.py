@@ -341,6 +341,36 @@ def test_fwd_long_ragged_sampled_rows(causal):
     check_fwd(og, lg, oref, lref, f"long ragged N={w.N} causal={causal}")
 
 
+@pytest.mark.parametrize("B,H,N", [(2, 20, 2000), (3, 7, 4000)])
+def test_fwd_causal_more_blocks_than_cus(B, H, N):
+    """Causal d = 128 grids with more 256-row query blocks than compute units
+    (320 and 336 blocks; H = 7 is no multiple of the 8 XCDs, so the work
+    order takes its plain rank-major form).  A block's result may not depend
+    on the grid around it: the same heads in groups of exactly 256 blocks
+    (the last group padded with repeats) must give bitwise the same O and L.
+    64 seeded rows of every head against the oracle."""
+    w = I.Workload(f"fwd_many_blocks_{B}_{H}_{N}", 1400 + H, B, H, N, 128, True, "bf16")
+    t = I.make_inputs(w)
+    say(f"causal more blocks than CUs B={B} H={H} N={N}")
+    q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
+    o, l = fa.forward(q, k, v, causal=True)
+    BH, per = B * H, 256 // ((N + 255) // 256)
+    qf, kf, vf = (x.reshape(1, BH, N, 128) for x in (q, k, v))
+    of, lf = o.reshape(BH, N, 128), l.reshape(BH, N)
+    for s in range(0, BH, per):
+        idx = list(range(s, min(s + per, BH)))
+        idx += [idx[-1]] * (per - len(idx))
+        o1, l1 = fa.forward(qf[:, idx].contiguous(), kf[:, idx].contiguous(), vf[:, idx].contiguous(), causal=True)
+        for j, hh in enumerate(idx):
+            assert torch.equal(o1[0, j], of[hh]) and torch.equal(l1[0, j], lf[hh]), (s, hh)
+    o, l = o.cpu().numpy(), l.cpu().numpy()
+    rows = lambda b, h: I.sample_rows(N, 64, 1400 + 10 * b + h)
+    oref, lref = oracle_fwd(t, True, 1 / math.sqrt(128), rows=rows)
+    og = np.stack([np.stack([o[b, h][rows(b, h)] for h in range(H)]) for b in range(B)])
+    lg = np.stack([np.stack([l[b, h][rows(b, h)] for h in range(H)]) for b in range(B)])
+    check_fwd(og, lg, oref, lref, f"more blocks than CUs B={B} H={H} N={N}")
+
+
 # ------------------------------------------------------------------ invariants and edge cases
 def test_fwd_uniform_scores_give_mean_of_values():
     """Q = 0: every visible key has weight 1/count (closed form)."""
@@ -393,12 +423,13 @@ def _rising_scores(B, H, N, gap_log2, seed, v_scale=1.0, d=128, dv=None):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("B,H,N", [(1, 2, 2048), (1, 64, 1024)])
+@pytest.mark.parametrize("B,H,N", [(1, 2, 2048), (1, 64, 1024), (1, 72, 1024)])
 @pytest.mark.parametrize("gap", [60.0, 110.0, 400.0])
 def test_fwd_d128_scores_rising_along_keys(B, H, N, gap, causal):
     """Weights far above 1 relative to a row's first keys: gaps that stay
     finite in float32 and one that overflows it.  Both must match the
-    oracle."""
+    oracle.  The grids: two key ranges per workgroup (2 heads), 256 blocks
+    of 256 rows, and 288 blocks (more than compute units)."""
     t = _rising_scores(B, H, N, gap, 310)
     o, l = run_fwd(t, causal)
     oref, lref = oracle_fwd(t, causal, 1 / math.sqrt(128))
