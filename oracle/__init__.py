@@ -41,8 +41,9 @@ Functions and what pins each one (tests/test_oracle.py):
                       element; keep rate, p = 0, the expectation of the
                       output, finite differences and the D identity pin the
                       forward and backward (tests/test_oracle_dropout.py).
-  varlen (module)     packed variable-length sequences ("Padding is silent
-                      waste", first page): per-sequence plain attention,
+  varlen (module)     packed variable-length sequences (the tip on PyTorch
+                      calls under "What it doesn't solve", first page:
+                      padded rows cost work): per-sequence plain attention,
                       pinned against one masked softmax over the whole packed
                       axis and its torch autograd (tests/test_oracle_varlen.py).
 """
