@@ -76,6 +76,8 @@ def library():
         i64p = ctypes.POINTER(ctypes.c_int64)
         lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, f, i, vp]
         lib.fa_fwd_strided.restype = i
+        lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        lib.fa_bwd_ex.restype = i
         lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd_noalloc.restype = i
         lib.fa_dropout_applied_p.argtypes = [f]
@@ -211,8 +213,10 @@ def forward_splitkv(q, k, v, causal=False, scale=None, n_splits=0, workspace=Non
     return o, l
 
 
-def _check_bwd(q, k, v, o, lse, do):
-    _check(q, k, v)
+def _check_bwd(q, k, v, o, lse, do, square=True):
+    _check(q, k, v, square=square)
+    if v.shape[3] != q.shape[3]:
+        raise ValueError(f"backward: v needs the width of q and k (dv = d), got {tuple(v.shape)} for d = {q.shape[3]}")
     if q.dtype != torch.bfloat16 or do.dtype != torch.bfloat16:
         raise TypeError("backward takes bfloat16 Q, K, V and dO")
     if do.shape != q.shape or o.shape != q.shape or lse.shape != q.shape[:3]:
@@ -248,21 +252,28 @@ def workspace_for(q, workspace=None):
 
 
 def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
-    """Gradients (dQ, dK, dV), float32 [B,H,N,d], of sum(dO * O).
+    """Gradients (dQ [B,H,Nq,d], dK and dV [B,H,Nk,d], float32) of sum(dO * O).
 
     ``o`` and ``lse`` must be the forward's outputs for the same inputs; the
-    probability tiles are recomputed from them.  bf16 inputs only.
+    probability tiles are recomputed from them.  bf16 inputs only.  Q may
+    have a different number of rows than K and V (fa_bwd_ex, upper-left
+    causal mask), V the width of Q and K.
     """
-    _check_bwd(q, k, v, o, lse, do)
-    B, H, N, d = q.shape
+    _check_bwd(q, k, v, o, lse, do, square=False)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
     workspace = workspace_for(q, workspace)
-    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-    dk = torch.empty_like(dq)
-    dv = torch.empty_like(dq)
-    st = library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-                          _ptr(workspace), B, H, N, d, _scale(scale, d), int(bool(causal)), _stream(q.device))
+    dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace))
+    tail = (_scale(scale, d), int(bool(causal)), _stream(q.device))
+    if Nq == Nk:
+        name, st = "fa_bwd", library().fa_bwd(*args, B, H, Nq, d, *tail)
+    else:
+        name, st = "fa_bwd_ex", library().fa_bwd_ex(*args, B, H, Nq, Nk, d, *tail)
     if st != FA_OK:
-        raise FAError("fa_bwd", st)
+        raise FAError(name, st)
     return dq, dk, dv
 
 

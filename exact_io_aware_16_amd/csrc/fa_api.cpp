@@ -226,7 +226,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const fl
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (!workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
-                                        N, d, scale, causal, nullptr, nullptr, stream));
+                                        N, N, d, scale, causal, nullptr, nullptr, stream));
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+              float* dq, float* dk, float* dv, void* workspace, int B, int H, int Nq, int Nk, int d, float scale,
+              int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape_ex(B, H, Nq, Nk, d, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  // nothing to write only when there are neither query rows nor keys; with
+  // keys but no query rows dK = dV = 0, with rows but no keys dQ = 0
+  if (B == 0 || H == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
+  if (Nq > 0 && (!q || !o || !lse || !dout || !dq)) return FA_ERR_NULL;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL;
+  if (Nq > 0 && Nk > 0 && (!q || !k || !v)) return FA_ERR_NULL;
+  if (Nq > 0 && Nk > 0 && !workspace) return FA_ERR_WORKSPACE;
+  return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
+                                        Nq, Nk, d, scale, causal, nullptr, nullptr, stream));
 }
 
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
@@ -242,8 +260,8 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const float* o, 
     return FA_ERR_SCRATCH;
   float* ws = nullptr;
   if (fa::scratch_on_current_device(&ws) != hipSuccess) return FA_ERR_HIP;
-  return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, ws, B * H, N, d, scale, causal, nullptr,
-                                        nullptr, stream));
+  return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, ws, B * H, N, N, d, scale, causal,
+                                        nullptr, nullptr, stream));
 }
 
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
@@ -259,7 +277,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, 
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (!workspace) return FA_ERR_WORKSPACE;
   return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
-                                        N, d, scale, causal, active ? &dp : nullptr, nullptr, stream));
+                                        N, N, d, scale, causal, active ? &dp : nullptr, nullptr, stream));
 }
 
 int fa_bwd_prep(const void* dout, const float* o, const float* lse, void* workspace, int B, int H, int N, int d,
@@ -283,7 +301,7 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
   if (empty) return FA_OK;
   if (!q || !k || !v || !dout || !dk || !dv) return FA_ERR_NULL;
   if (!workspace) return FA_ERR_WORKSPACE;
-  return hip_status(fa::launch_bwd_dkdv(q, k, v, dout, static_cast<const float*>(workspace), dk, dv, B * H, N, d,
+  return hip_status(fa::launch_bwd_dkdv(q, k, v, dout, static_cast<const float*>(workspace), dk, dv, B * H, N, N, d,
                                         scale, causal, nullptr, nullptr, stream));
 }
 
@@ -299,7 +317,8 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
   const float* ws = static_cast<const float*>(workspace);
   const size_t rows = (size_t)B * (size_t)H * (size_t)N;
   return hip_status(
-      fa::launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, B * H, N, d, scale, causal, nullptr, nullptr, stream));
+      fa::launch_bwd_dq_bf16(q, k, v, dout, ws + rows, ws, dq, B * H, N, N, d, scale, causal, nullptr, nullptr,
+                             stream));
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse, const int* cu_seqlens, int B,
@@ -327,7 +346,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const float* o, c
   if (!workspace) return FA_ERR_WORKSPACE;
   const fa::Seqs sq{cu_seqlens, H, total};
   return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
-                                        max_seqlen, d, scale, causal, nullptr, &sq, stream));
+                                        max_seqlen, max_seqlen, d, scale, causal, nullptr, &sq, stream));
 }
 
 const char* fa_status_string(int status) {

@@ -126,7 +126,7 @@ template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     const bf16_raw* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dsc,
-    float* __restrict__ dK, float* __restrict__ dV, int N, int n_kvblk, int total, float scale, float c,
+    float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, int n_kvblk, int total, float scale, float c,
     Dropout drop, Seqs seqs) {
   constexpr int NKK = D / 16;  // 16-wide head-dim slices (contraction of S and dP)
   constexpr int NDB = D / 32;  // 32-row blocks of dK^T / dV^T
@@ -149,28 +149,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
-  // first row of this head; for packed sequences, of sequence b = bh / H in
-  // head h = bh % H (then N is that sequence's length and n_kvblk covers the
-  // longest one)
-  size_t row0 = (size_t)bh * N;
+  // first query row (Q, dO, statistics) and first key row (K, V, dK, dV) of
+  // this head; for packed sequences, of sequence b = bh / H in head h = bh % H
+  // (then Nq = Nk is that sequence's length and n_kvblk covers the longest
+  // one)
+  size_t row0 = (size_t)bh * Nq, krow0 = (size_t)bh * Nk;
   if (seqs.cu) {
     const int b = bh / seqs.H, hh = bh - b * seqs.H;
     int s0, s1;
     seq_range(seqs, b, s0, s1);
-    N = s1 - s0;
-    row0 = (size_t)hh * seqs.total + s0;
-    if (kvb * kBKV >= N) return;  // past the end of a shorter sequence
+    Nq = Nk = s1 - s0;
+    row0 = krow0 = (size_t)hh * seqs.total + s0;
+    if (kvb * kBKV >= Nk) return;  // past the end of a shorter sequence
   }
-  const size_t head = row0 * D;
+  const size_t head = row0 * D, khead = krow0 * D;
 
   const int k0 = kvb * kBKV;
   const int my_key = k0 + 32 * wave + col;
 
-  const int head_bytes = N * D * 2;
+  const int q_first = CAUSAL ? k0 : 0;  // k0 is a multiple of kBQ
+  const int n_steps = (Nq - q_first + kBQ - 1) / kBQ;
+  if (n_steps <= 0) {
+    // no query row sees these keys (causal, Nq <= k0): zero gradients
+    if (my_key < Nk) {
+      float* dKrow = dK + khead + (size_t)my_key * D;
+      float* dVrow = dV + khead + (size_t)my_key * D;
+#pragma unroll
+      for (int d4 = 0; d4 < D / 8; ++d4) {
+        *reinterpret_cast<float4*>(dKrow + 8 * d4 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(dVrow + 8 * d4 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    return;  // workgroup-uniform: every wave leaves before any barrier
+  }
+
+  const int head_bytes = Nq * D * 2, khead_bytes = Nk * D * 2;
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + head), (short)0, head_bytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + khead), (short)0, khead_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + head), (short)0, head_bytes, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + khead), (short)0, khead_bytes, 0x00020000);
 
   QCopy<D> qc;
   qc.init(wave, lane);
@@ -196,19 +213,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
     if (wave_s < 2) {
       const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((wave_s == 0 ? L2 : Dsc) + row0 + q0), (short)0, (N - q0) * 4, 0x00020000);
+          (void*)((wave_s == 0 ? L2 : Dsc) + row0 + q0), (short)0, (Nq - q0) * 4, 0x00020000);
       lds_copy4(rt, (uint32_t)lane * 4u, 0u, lds_addr_of(wave_s == 0 ? sm.l2[b] : sm.dsc[b]));
     }
   };
-
-  const int q_first = CAUSAL ? k0 : 0;  // k0 is a multiple of kBQ
-  const int n_steps = (N - q_first + kBQ - 1) / kBQ;
 
   issue_qtile(0u, q_first);
 
   // K and V rows of this wave's keys, 8 head-dim elements per k-slice: the
   // B operands of S = Q K^T and dP = dO V^T for the whole kernel (rows past
-  // N read as zero)
+  // Nk read as zero)
   bf16x8 kres[NKK], vres[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
@@ -407,10 +421,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       if constexpr (h == 0) load_ld(x, qb, ic<1>{});
       else if (has_next) load_ld(xn, qbn, ic<0>{});
       // masked pairs of this chunk: e < dead (row q0 + 32 qb + 16 h + 8 g + e
-      // sees key my_key iff my_key <= that row, and only keys below N exist)
+      // sees key my_key iff my_key <= that row, and only keys below Nk exist)
       if constexpr (M) {
         dead = CAUSAL ? my_key - (x.q0 + 32 * qb + 16 * h + 8 * g) : 0;
-        dead = my_key >= N ? 8 : dead;
+        dead = my_key >= Nk ? 8 : dead;
       }
     }
 #pragma unroll
@@ -536,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // st touches steps st and st+1, so it needs masks iff st < n_mask.  Two
   // loops rather than a branch per iteration keep one register assignment
   // per loop body.
-  const int n_mask = k0 + kBKV > N ? n_steps : CAUSAL ? min(n_steps, (k0 + kBKV - q_first + kBQ - 1) / kBQ) : 0;
+  const int n_mask = k0 + kBKV > Nk ? n_steps : CAUSAL ? min(n_steps, (k0 + kBKV - q_first + kBQ - 1) / kBQ) : 0;
   int st = 0;
   for (; st + 1 < n_steps && st < n_mask; ++st) step(st, with_masks);
   // mask-free steps three at a time from a multiple of 3: tile st + i in buffer i
@@ -578,9 +592,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
   group_fence();  // nothing after this point is scheduled above the pins
 
-  if (my_key < N) {
-    float* dKrow = dK + head + (size_t)my_key * D;
-    float* dVrow = dV + head + (size_t)my_key * D;
+  if (my_key < Nk) {
+    float* dKrow = dK + khead + (size_t)my_key * D;
+    float* dVrow = dV + khead + (size_t)my_key * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -607,25 +621,26 @@ hipError_t launch_prep(const void* dout, const float* o, const float* lse, float
   return hipGetLastError();
 }
 
-// BH, N: heads and sequence length; for packed sequences the B * H
-// (sequence, head) units and the longest length, the workspace then holding
-// H * total rows.
-long long workspace_rows(int BH, int N, const Seqs& sq) {
-  return sq.cu ? (long long)sq.H * sq.total : (long long)BH * N;
+// BH, Nq: heads and query rows; for packed sequences the B * H (sequence,
+// head) units and the longest length, the workspace then holding H * total
+// rows.
+long long workspace_rows(int BH, int Nq, const Seqs& sq) {
+  return sq.cu ? (long long)sq.H * sq.total : (long long)BH * Nq;
 }
 
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws, float* dk,
-                       float* dv, int BH, int N, float scale, const Dropout& drop, const Seqs& sq,
+                       float* dv, int BH, int Nq, int Nk, float scale, const Dropout& drop, const Seqs& sq,
                        hipStream_t stream) {
-  const long long rows = workspace_rows(BH, N, sq);
-  const int n_kvblk = (N + kBKV - 1) / kBKV;
+  const long long rows = workspace_rows(BH, Nq, sq);
+  const int n_kvblk = (Nk + kBKV - 1) / kBKV;
   const long long total = (long long)BH * n_kvblk;
+  if (total == 0) return hipSuccess;  // no keys: no dK, dV
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROP>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k), static_cast<const bf16_raw*>(v),
-                     static_cast<const bf16_raw*>(dout), ws + rows, ws, dk, dv, N, n_kvblk, (int)total, scale,
+                     static_cast<const bf16_raw*>(dout), ws + rows, ws, dk, dv, Nq, Nk, n_kvblk, (int)total, scale,
                      scale * kLog2e, drop, sq);
   return hipGetLastError();
 }
@@ -640,38 +655,39 @@ hipError_t launch_bwd_prep(const void* dout, const float* o, const float* lse, f
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_drop(const void* q, const void* k, const void* v, const void* dout, const float* ws,
-                            float* dk, float* dv, int BH, int N, float scale, const Dropout* drop, const Seqs& sq,
-                            hipStream_t stream) {
+                            float* dk, float* dv, int BH, int Nq, int Nk, float scale, const Dropout* drop,
+                            const Seqs& sq, hipStream_t stream) {
   if (drop) {
     if (sq.cu) return hipErrorInvalidValue;  // dropout is offered for the dense layout only
-    return launch_dkdv<D, CAUSAL, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, *drop, sq, stream);
+    return launch_dkdv<D, CAUSAL, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, *drop, sq, stream);
   }
-  return launch_dkdv<D, CAUSAL, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, Dropout{}, sq, stream);
+  return launch_dkdv<D, CAUSAL, false>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, Dropout{}, sq, stream);
 }
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws,
-                           float* dk, float* dv, int BH, int N, int d, float scale, int causal, const Dropout* drop,
-                           const Seqs* seqs, hipStream_t stream) {
+                           float* dk, float* dv, int BH, int Nq, int Nk, int d, float scale, int causal,
+                           const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
   const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
   if (d == 128)
-    return causal ? launch_dkdv_drop<128, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, sq, stream)
-                  : launch_dkdv_drop<128, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, sq, stream);
-  return causal ? launch_dkdv_drop<64, true>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, sq, stream)
-                : launch_dkdv_drop<64, false>(q, k, v, dout, ws, dk, dv, BH, N, scale, drop, sq, stream);
+    return causal ? launch_dkdv_drop<128, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, stream)
+                  : launch_dkdv_drop<128, false>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, stream);
+  return causal ? launch_dkdv_drop<64, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, stream)
+                : launch_dkdv_drop<64, false>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
-                           const void* dout, float* dq, float* dk, float* dv, float* ws, int BH, int N, int d,
-                           float scale, int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+                           const void* dout, float* dq, float* dk, float* dv, float* ws, int BH, int Nq, int Nk,
+                           int d, float scale, int causal, const Dropout* drop, const Seqs* seqs,
+                           hipStream_t stream) {
   const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
-  const long long rows = workspace_rows(BH, N, sq);
+  const long long rows = workspace_rows(BH, Nq, sq);
   // The dQ pass computes the row statistics of its own rows (the
   // preprocess, fused: every row belongs to exactly one of its workgroups)
   // and stores them for the dK/dV pass, which runs after it on the stream.
-  hipError_t e = launch_bwd_dq_fused(q, k, v, dout, o, lse, ws + rows, ws, dq, BH, N, d, scale, causal, drop, seqs,
-                                     stream);
+  hipError_t e = launch_bwd_dq_fused(q, k, v, dout, o, lse, ws + rows, ws, dq, BH, Nq, Nk, d, scale, causal, drop,
+                                     seqs, stream);
   if (e != hipSuccess) return e;
-  return launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, N, d, scale, causal, drop, seqs, stream);
+  return launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, d, scale, causal, drop, seqs, stream);
 }
 
 }  // namespace fa

@@ -84,8 +84,8 @@ template <int D, bool CAUSAL, bool DROP, bool FUSED>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     const bf16_raw* __restrict__ dO, float* __restrict__ L2, float* __restrict__ Dsc, const float* __restrict__ O,
-    const float* __restrict__ LSE, float* __restrict__ dQ, int N, int n_qblk, int total, float scale, float c,
-    Dropout drop, Seqs seqs) {
+    const float* __restrict__ LSE, float* __restrict__ dQ, int Nq, int Nk, int n_qblk, int total, float scale,
+    float c, Dropout drop, Seqs seqs) {
   constexpr int BC = DqTile<D>::BC;
   constexpr int NKB = BC / 32;  // 32-key blocks per tile
   constexpr int NKK = D / 16;   // 16-wide head-dim slices (contraction of S and dP)
@@ -110,27 +110,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
-  // first row of this head; for packed sequences, of sequence b = bh / H in
-  // head h = bh % H (then N is that sequence's length and n_qblk covers the
-  // longest one)
-  size_t row0 = (size_t)bh * N;
+  // first query row (Q, dO, O, statistics, dQ) and first key row (K, V) of
+  // this head; for packed sequences, of sequence b = bh / H in head h = bh % H
+  // (then Nq = Nk is that sequence's length and n_qblk covers the longest
+  // one)
+  size_t row0 = (size_t)bh * Nq, krow0 = (size_t)bh * Nk;
   if (seqs.cu) {
     const int b = bh / seqs.H, hh = bh - b * seqs.H;
     int s0, s1;
     seq_range(seqs, b, s0, s1);
-    N = s1 - s0;
-    row0 = (size_t)hh * seqs.total + s0;
-    if (qblk * kBR >= N) return;  // past the end of a shorter sequence
+    Nq = Nk = s1 - s0;
+    row0 = krow0 = (size_t)hh * seqs.total + s0;
+    if (qblk * kBR >= Nq) return;  // past the end of a shorter sequence
   }
-  const size_t head = row0 * D;
+  const size_t head = row0 * D, khead = krow0 * D;
 
   const int q_start = qblk * kBR;
   const int q0w = q_start + 32 * wave;
   const int my_q = q0w + col;
-  const int kv_end = CAUSAL ? min(N, q_start + kBR) : N;
+  // keys some row of the workgroup sees (upper-left causal mask): at least
+  // key 0, since Nk >= 1 on every launch
+  const int kv_end = CAUSAL ? min(Nk, q_start + kBR) : Nk;
   const int n_tiles = (kv_end + BC - 1) / BC;
+  if (n_tiles == 0) {
+    // no keys at all (Nk == 0): dQ = 0.  Workgroup-uniform, before any copy
+    // or barrier; the statistics are not needed (no dK / dV rows exist).
+    if (my_q < Nq) {
+      float* row = dQ + head + (size_t)my_q * D;
+#pragma unroll
+      for (int d4 = 0; d4 < D / 8; ++d4)
+        *reinterpret_cast<float4*>(row + 8 * d4 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
 
-  const int head_bytes = N * D * 2;
+  const int head_bytes = Nk * D * 2;
   KvCopy<D> kc;
   kc.init(wave, lane);
   // the wave index in a scalar register: the copies' LDS addresses (M0) are
@@ -143,9 +157,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     key0 = __builtin_amdgcn_readfirstlane(key0);
     const uint32_t rest = (uint32_t)head_bytes - (uint32_t)key0 * D * 2;
     const __amdgpu_buffer_rsrc_t kt =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(K + head + (size_t)key0 * D), (short)0, (int)rest, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + khead + (size_t)key0 * D), (short)0, (int)rest, 0x00020000);
     const __amdgpu_buffer_rsrc_t vt =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(V + head + (size_t)key0 * D), (short)0, (int)rest, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + khead + (size_t)key0 * D), (short)0, (int)rest, 0x00020000);
     const uint32_t kb = lds_addr_of(sm.k[b]), vb = lds_addr_of(sm.v[b]);
 #pragma unroll
     for (int i = 0; i < KvCopy<D>::INSTR; ++i) {
@@ -159,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   bf16x8 qf[NKK], dof[NKK];
   float l2q, dq_sc;
   {
-    const int qr = min(my_q, N - 1);
+    const int qr = min(my_q, Nq - 1);
     const bf16_raw* Qrow = Q + head + (size_t)qr * D;
     const bf16_raw* Grow = dO + head + (size_t)qr * D;
 #pragma unroll
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
         for (int kk = 0; kk < sft; ++kk) part[kk] = part[kk] + part[kk + sft];
       dq_sc = scale * halves_sum(part[0]);
       l2q = lse_q * kLog2e;
-      if (g == 0 && my_q < N) {
+      if (g == 0 && my_q < Nq) {
         Dsc[row0 + my_q] = dq_sc;
         L2[row0 + my_q] = l2q;
       }
@@ -264,7 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int sw_t = swz<RB>(tr_row);
   const uint32_t tk_lane = (uint32_t)(tr_row * RB + 64 * (sw_t >> 2) + 16 * (c0 ^ (sw_t & 3)) + 8 * (sl & 1));
   const uint32_t k_base0 = lds_addr_of(sm.k[0]);
-  const int last_key = CAUSAL ? min(my_q, N - 1) : N - 1;  // keys above are masked
+  const int last_key = CAUSAL ? min(my_q, Nk - 1) : Nk - 1;  // keys above are masked
 
   // per-tile context: LDS addresses in the tile's buffer, first key
   struct Tile {
@@ -475,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   // Tiles that need masks (for any row of the workgroup) form a suffix: the
   // ones that meet the diagonal and the one holding the end of the sequence.
   // Iteration t touches tiles t and t+1, so it needs masks iff t+1 >= t_mask.
-  const int t_mask = min(CAUSAL ? (q_start + 1) / BC : n_tiles, N / BC);
+  const int t_mask = min(CAUSAL ? (q_start + 1) / BC : n_tiles, Nk / BC);
   int t = 0;
   // mask-free tiles three at a time from t = 0: tile t + i in buffer i
   for (; t + 3 < n_tiles && t + 3 < t_mask; t += 3) {
@@ -524,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   }
   group_fence();  // nothing after this point is scheduled above the pins
 
-  if (my_q < N) {
+  if (my_q < Nq) {
     float* row = dQ + head + (size_t)my_q * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -539,61 +553,62 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 // l2 / dsc); else l2 / dsc hold them already
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch(const void* q, const void* k, const void* v, const void* dout, float* l2, float* dsc,
-                  const float* o, const float* lse, float* dq, int BH, int N, float scale, const Dropout& drop,
-                  const Seqs& sq, hipStream_t stream) {
-  const int n_qblk = (N + kBR - 1) / kBR;
+                  const float* o, const float* lse, float* dq, int BH, int Nq, int Nk, float scale,
+                  const Dropout& drop, const Seqs& sq, hipStream_t stream) {
+  const int n_qblk = (Nq + kBR - 1) / kBR;
   const long long total = (long long)BH * n_qblk;
+  if (total == 0) return hipSuccess;  // no query rows: no dQ
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
   if (o)
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP, true>), dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
-                       static_cast<const bf16_raw*>(v), static_cast<const bf16_raw*>(dout), l2, dsc, o, lse, dq, N,
-                       n_qblk, (int)total, scale, scale * kLog2e, drop, sq);
+                       static_cast<const bf16_raw*>(v), static_cast<const bf16_raw*>(dout), l2, dsc, o, lse, dq, Nq,
+                       Nk, n_qblk, (int)total, scale, scale * kLog2e, drop, sq);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP, false>), dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
-                       static_cast<const bf16_raw*>(v), static_cast<const bf16_raw*>(dout), l2, dsc, o, lse, dq, N,
-                       n_qblk, (int)total, scale, scale * kLog2e, drop, sq);
+                       static_cast<const bf16_raw*>(v), static_cast<const bf16_raw*>(dout), l2, dsc, o, lse, dq, Nq,
+                       Nk, n_qblk, (int)total, scale, scale * kLog2e, drop, sq);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_drop(const void* q, const void* k, const void* v, const void* dout, float* l2, float* dsc,
-                       const float* o, const float* lse, float* dq, int BH, int N, float scale, const Dropout* drop,
-                       const Seqs& sq, hipStream_t stream) {
+                       const float* o, const float* lse, float* dq, int BH, int Nq, int Nk, float scale,
+                       const Dropout* drop, const Seqs& sq, hipStream_t stream) {
   if (drop) {
     if (sq.cu) return hipErrorInvalidValue;  // dropout is offered for the dense layout only
-    return launch<D, CAUSAL, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, *drop, sq, stream);
+    return launch<D, CAUSAL, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, *drop, sq, stream);
   }
-  return launch<D, CAUSAL, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, Dropout{}, sq, stream);
+  return launch<D, CAUSAL, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, Dropout{}, sq, stream);
 }
 
 hipError_t launch_any(const void* q, const void* k, const void* v, const void* dout, float* l2, float* dsc,
-                      const float* o, const float* lse, float* dq, int BH, int N, int d, float scale, int causal,
-                      const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+                      const float* o, const float* lse, float* dq, int BH, int Nq, int Nk, int d, float scale,
+                      int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
   const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
   if (d == 128)
-    return causal ? launch_drop<128, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, drop, sq, stream)
-                  : launch_drop<128, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, drop, sq, stream);
-  return causal ? launch_drop<64, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, drop, sq, stream)
-                : launch_drop<64, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, scale, drop, sq, stream);
+    return causal ? launch_drop<128, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, stream)
+                  : launch_drop<128, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, stream);
+  return causal ? launch_drop<64, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, stream)
+                : launch_drop<64, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
-                              const float* dsc, float* dq, int BH, int N, int d, float scale, int causal,
+                              const float* dsc, float* dq, int BH, int Nq, int Nk, int d, float scale, int causal,
                               const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
   // statistics only read on this launch
-  return launch_any(q, k, v, dout, const_cast<float*>(l2), const_cast<float*>(dsc), nullptr, nullptr, dq, BH, N, d,
-                    scale, causal, drop, seqs, stream);
+  return launch_any(q, k, v, dout, const_cast<float*>(l2), const_cast<float*>(dsc), nullptr, nullptr, dq, BH, Nq,
+                    Nk, d, scale, causal, drop, seqs, stream);
 }
 
 hipError_t launch_bwd_dq_fused(const void* q, const void* k, const void* v, const void* dout, const float* o,
-                               const float* lse, float* l2, float* dsc, float* dq, int BH, int N, int d, float scale,
-                               int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
-  return launch_any(q, k, v, dout, l2, dsc, o, lse, dq, BH, N, d, scale, causal, drop, seqs, stream);
+                               const float* lse, float* l2, float* dsc, float* dq, int BH, int Nq, int Nk, int d,
+                               float scale, int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+  return launch_any(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, d, scale, causal, drop, seqs, stream);
 }
 
 }  // namespace fa

@@ -57,24 +57,25 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           int d, float scale, int causal, hipStream_t stream);
 
 // dQ only, query-stationary (fa_bwd_dq.hip); l2 and dsc are the per-row
-// L log2(e) and scale * D written by the backward preprocess.
+// L log2(e) and scale * D written by the backward preprocess.  Nq query rows
+// and Nk keys per head (upper-left causal mask when they differ).
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
-                              const float* dsc, float* dq, int BH, int N, int d, float scale, int causal,
+                              const float* dsc, float* dq, int BH, int Nq, int Nk, int d, float scale, int causal,
                               const Dropout* drop, const Seqs* seqs, hipStream_t stream);
 // The dQ pass with the preprocess fused in: computes scale D = scale dO . O and
 // L log2(e) of its rows from o and lse (bitwise as launch_bwd_prep does),
 // stores them to l2 / dsc for a dK/dV launch that follows, and writes dq.
 hipError_t launch_bwd_dq_fused(const void* q, const void* k, const void* v, const void* dout, const float* o,
-                               const float* lse, float* l2, float* dsc, float* dq, int BH, int N, int d, float scale,
-                               int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream);
+                               const float* lse, float* l2, float* dsc, float* dq, int BH, int Nq, int Nk, int d,
+                               float scale, int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream);
 
-// Backward phases (fa_bwd.hip); ws holds [scale * D | L log2(e)], BH * N
-// floats each.
+// Backward phases (fa_bwd.hip); ws holds [scale * D | L log2(e)], one float
+// each per query row (BH * Nq).  The preprocess works on query rows only.
 hipError_t launch_bwd_prep(const void* dout, const float* o, const float* lse, float* ws, int BH, int N, int d,
                            float scale, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws,
-                           float* dk, float* dv, int BH, int N, int d, float scale, int causal, const Dropout* drop,
-                           const Seqs* seqs, hipStream_t stream);
+                           float* dk, float* dv, int BH, int Nq, int Nk, int d, float scale, int causal,
+                           const Dropout* drop, const Seqs* seqs, hipStream_t stream);
 
 // The allocation-free backward's scratch (fa_scratch.hip): its capacity in
 // floats, and its device address on the current device (looked up once per
@@ -83,7 +84,7 @@ size_t scratch_floats();
 hipError_t scratch_on_current_device(float** out);
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
-                           const void* dout, float* dq, float* dk, float* dv, float* dvec, int BH, int N,
+                           const void* dout, float* dq, float* dk, float* dv, float* dvec, int BH, int Nq, int Nk,
                            int d, float scale, int causal, const Dropout* drop, const Seqs* seqs,
                            hipStream_t stream);
 

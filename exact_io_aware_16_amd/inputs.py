@@ -93,13 +93,17 @@ def make_inputs(w: Workload, with_do=None):
     return out
 
 
-def make_general(B, H, Nq, Nk, d, dv, seed, std=1.0):
+def make_general(B, H, Nq, Nk, d, dv, seed, std=1.0, with_do=False):
     """Seeded bf16 Q [B,H,Nq,d], K [B,H,Nk,d], V [B,H,Nk,dv] (CPU tensors) for
-    the general forward contract; seeds 1000*seed + {q:1, k:2, v:3}."""
+    the general forward contract, and dO [B,H,Nq,dv] when with_do; seeds
+    1000*seed + {q:1, k:2, v:3, do:4}."""
     base = 1000 * int(seed)
-    return {"q": draw((B, H, Nq, d), base + _TENSOR_SEED["q"], std),
-            "k": draw((B, H, Nk, d), base + _TENSOR_SEED["k"], std),
-            "v": draw((B, H, Nk, dv), base + _TENSOR_SEED["v"])}
+    t = {"q": draw((B, H, Nq, d), base + _TENSOR_SEED["q"], std),
+         "k": draw((B, H, Nk, d), base + _TENSOR_SEED["k"], std),
+         "v": draw((B, H, Nk, dv), base + _TENSOR_SEED["v"])}
+    if with_do:
+        t["do"] = draw((B, H, Nq, dv), base + _TENSOR_SEED["do"])
+    return t
 
 
 # Decoding: one query row per head against a long key sequence (split-KV).

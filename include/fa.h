@@ -172,6 +172,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const float* o, const fl
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
+ * fa_bwd for Nq query rows against Nk keys per head: the backward of fa_fwd_ex
+ * with dv = d ("Build it": the query and key lengths may differ, and the
+ * causal mask is anchored at the upper left, so row i sees keys j <= i).
+ *   q, dout       : device, bf16 [B,H,Nq,d];  k, v : device, bf16 [B,H,Nk,d]
+ *   o, lse        : device, float32 [B,H,Nq,d] and [B,H,Nq], as written by
+ *                   fa_fwd_ex for the same inputs (dv = d)
+ *   dq            : device, float32 [B,H,Nq,d];  dk, dv : float32 [B,H,Nk,d]
+ *                   -- all fully overwritten
+ *   workspace     : device, >= fa_bwd_workspace_bytes(B,H,Nq,d) bytes; may
+ *                   be NULL when Nq or Nk is 0
+ * A key that no query row sees (causal, j >= Nq) gets dk = dv = 0; with
+ * Nk = 0, dq = 0; with Nq = 0, dk = dv = 0.  Pointers of tensors with no
+ * elements may be NULL.  B, H, Nq or Nk negative, or B*H*max(Nq,Nk)*d past
+ * the addressable range: FA_ERR_SHAPE.  d outside {64, 128}: FA_ERR_HEADDIM.
+ * Same kernels, stream behaviour and determinism as fa_bwd (which is this
+ * call with Nq = Nk).
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse,
+              const void* dout, float* dq, float* dk, float* dv, void* workspace,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream);
+
+/*
  * fa_bwd without a workspace argument, for callers that cannot allocate
  * device memory (code being captured into a HIP graph, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, layouts, results and

@@ -63,6 +63,10 @@ int fwd_ex(int B, int H, int Nq, int Nk, int d, int dv, float scale, int causal,
 int bwd(int B, int H, int N, int d, float scale, int causal, void* ws = P, float* dv = F) {
   return fa_bwd(P, P, P, F, F, P, F, F, dv, ws, B, H, N, d, scale, causal, nullptr);
 }
+int bwd_ex(int B, int H, int Nq, int Nk, int d, float scale, int causal, void* ws = P, float* dk = F,
+           const void* q = P) {
+  return fa_bwd_ex(q, P, P, F, F, P, F, dk, F, ws, B, H, Nq, Nk, d, scale, causal, nullptr);
+}
 int noalloc(int B, int H, int N, int d, float scale, int causal, float* dq = F) {
   return fa_bwd_noalloc(P, P, P, F, F, P, dq, F, F, B, H, N, d, scale, causal, nullptr);
 }
@@ -168,6 +172,24 @@ int main() {
   EXPECT_SIZE(fa_bwd_workspace_bytes(0, 16, 4096, 128), 0);
   EXPECT_SIZE(fa_bwd_workspace_bytes(1, 1, 10, 48), 0);
   EXPECT_SIZE(fa_bwd_workspace_bytes(INT_MAX, INT_MAX, INT_MAX, 128), 0);
+
+  // ---- backward with differing query and key counts
+  EXPECT(bwd_ex(1, 2, 8, 5, 96, 0.125f, 0), FA_ERR_HEADDIM);
+  EXPECT(bwd_ex(1, 2, -1, 5, 64, 0.125f, 0), FA_ERR_SHAPE);
+  EXPECT(bwd_ex(1, 2, 8, INT_MIN, 64, 0.125f, 0), FA_ERR_SHAPE);
+  EXPECT(bwd_ex(1, 2, 8, 5, 64, 0.125f, 2), FA_ERR_SHAPE);
+  EXPECT(bwd_ex(1, 2, 8, 5, 64, inf_f, 0), FA_ERR_SCALE);
+  EXPECT(bwd_ex(1, 2, 8, 5, 64, 0.125f, 0, nullptr), FA_ERR_WORKSPACE);
+  EXPECT(bwd_ex(1, 2, 8, 5, 64, 0.125f, 0, P, nullptr), FA_ERR_NULL);
+  EXPECT(bwd_ex(1, 2, 8, 5, 64, 0.125f, 0, P, F, nullptr), FA_ERR_NULL);
+  EXPECT(bwd_ex(1, 2, 0, 0, 64, 0.125f, 1, nullptr, nullptr, nullptr), FA_OK);
+  EXPECT(bwd_ex(0, 2, 8, 5, 64, 0.125f, 1, nullptr, nullptr, nullptr), FA_OK);
+  EXPECT(bwd_ex(1, 2, 0, 5, 64, 0.125f, 1, nullptr, F, nullptr), FA_ERR_HIP);   // no rows: dK = dV = 0 written
+  EXPECT(bwd_ex(1, 2, 0, 5, 64, 0.125f, 1, nullptr, nullptr, nullptr), FA_ERR_NULL);
+  EXPECT(bwd_ex(1, 2, 8, 0, 64, 0.125f, 0, nullptr, nullptr), FA_ERR_HIP);       // no keys: dQ = 0 written
+  EXPECT(bwd_ex(1, 2, 1 << 23, 5, 64, 0.125f, 0), FA_ERR_SHAPE);
+  EXPECT(bwd_ex(INT_MAX, INT_MAX, 8, 5, 128, 0.125f, 1), FA_ERR_SHAPE);
+  EXPECT(bwd_ex(2, 16, 4096, 1000, 128, 0.125f, 1), FA_ERR_HIP);
 
   // ---- the backward phases
   EXPECT(fa_bwd_prep(P, F, F, P, 1, 2, 8, 96, 0.1f, nullptr), FA_ERR_HEADDIM);

@@ -22,7 +22,7 @@ hipError_t launch_fwd_f32(const float*, const float*, const float*, float*, floa
 }
 
 hipError_t launch_bwd_dq_bf16(const void*, const void*, const void*, const void*, const float*, const float*, float*,
-                              int, int, int, float, int, const Dropout*, const Seqs*, hipStream_t) {
+                              int, int, int, int, float, int, const Dropout*, const Seqs*, hipStream_t) {
   ++g_launches;
   return hipErrorNotSupported;
 }
@@ -33,13 +33,13 @@ hipError_t launch_bwd_prep(const void*, const float*, const float*, float*, int,
 }
 
 hipError_t launch_bwd_dkdv(const void*, const void*, const void*, const void*, const float*, float*, float*, int, int,
-                           int, float, int, const Dropout*, const Seqs*, hipStream_t) {
+                           int, int, float, int, const Dropout*, const Seqs*, hipStream_t) {
   ++g_launches;
   return hipErrorNotSupported;
 }
 
 hipError_t launch_bwd_bf16(const void*, const void*, const void*, const float*, const float*, const void*, float*,
-                           float*, float*, float*, int, int, int, float, int, const Dropout*, const Seqs*,
+                           float*, float*, float*, int, int, int, int, float, int, const Dropout*, const Seqs*,
                            hipStream_t) {
   ++g_launches;
   return hipErrorNotSupported;

@@ -729,6 +729,74 @@ def test_fwdbwd_4k_d128_causal_full():
     check_bwd(got, oracle_bwd(t, w.causal, w.scale), w.name)
 
 
+# ------------------------------------------------------------------ backward, general shapes (fa_bwd_ex)
+def run_bwd_general(t, causal):
+    q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
+    o, l = fa.forward(q, k, v, causal=causal)
+    dq, dk, dv = fa.backward(q, k, v, o, l, do, causal=causal)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(100, 300), (300, 100), (1, 200), (200, 1), (129, 64), (64, 1000), (1000, 129)])
+def test_bwd_general_shapes(nq, nk, d, causal):
+    """Nq != Nk with the upper-left causal mask: every gradient element
+    against the oracle; keys past the last query row get exactly zero."""
+    t = I.make_general(2, 3, nq, nk, d, d, 7000 + nq + 3 * nk + d, with_do=True)
+    tag = f"bwd_ex Nq={nq} Nk={nk} d={d} causal={causal}"
+    say(tag)
+    got = run_bwd_general(t, causal)
+    ref = oracle_bwd(t, causal, 1 / math.sqrt(d))
+    check_bwd(got, ref, tag)
+    if causal and nk > nq:
+        assert np.all(got[1][:, :, nq:] == 0) and np.all(got[2][:, :, nq:] == 0), tag
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_bwd_ex_square_is_fa_bwd(d, causal):
+    """fa_bwd_ex with Nq = Nk runs exactly fa_bwd: bitwise equal gradients."""
+    t = shape_inputs(1, 2, 300, d, "bf16", 7100 + d, with_do=True)
+    q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
+    say(f"bwd_ex square d={d} causal={causal}")
+    o, l = fa.forward(q, k, v, causal=causal)
+    dq, dk, dv = fa.backward(q, k, v, o, l, do, causal=causal)
+    B, H, N, _ = q.shape
+    g = [torch.full_like(dq, 7.0) for _ in range(3)]
+    ws = fa.workspace_for(q)
+    ptr = lambda x: __import__("ctypes").c_void_p(x.data_ptr())
+    st = fa.library().fa_bwd_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(l), ptr(do), ptr(g[0]), ptr(g[1]), ptr(g[2]),
+                                ptr(ws), B, H, N, N, d, 1 / math.sqrt(d), int(causal), None)
+    torch.cuda.synchronize()
+    assert st == 0
+    for a_, b_ in zip((dq, dk, dv), g):
+        assert torch.equal(a_, b_)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ex_empty_sides(causal):
+    """No keys: dQ = 0.  No query rows: dK = dV = 0.  Outputs start at 7.0, so
+    each is seen to be written."""
+    ctypes = __import__("ctypes")
+    ptr = lambda x: ctypes.c_void_p(x.data_ptr()) if x is not None and x.numel() else None
+    lib = fa.library()
+    for nq, nk in ((50, 0), (0, 70)):
+        t = I.make_general(2, 3, nq, nk, 128, 128, 7200 + nq + nk, with_do=True)
+        q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "do"))
+        o = torch.zeros((2, 3, nq, 128), device="cuda")
+        l = torch.full((2, 3, nq), -math.inf, device="cuda")
+        dq = torch.full((2, 3, nq, 128), 7.0, device="cuda")
+        dk = torch.full((2, 3, nk, 128), 7.0, device="cuda")
+        dv = torch.full((2, 3, nk, 128), 7.0, device="cuda")
+        say(f"bwd_ex empty side Nq={nq} Nk={nk} causal={causal}")
+        st = lib.fa_bwd_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(l), ptr(do), ptr(dq), ptr(dk), ptr(dv), None,
+                           2, 3, nq, nk, 128, 0.125, int(causal), None)
+        torch.cuda.synchronize()
+        assert st == 0
+        assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+
+
 # ------------------------------------------------------------------ strided inputs (fa_fwd_strided)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])

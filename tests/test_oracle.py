@@ -257,6 +257,34 @@ def test_backward_matches_central_finite_differences(causal):
         assert np.max(np.abs(fd - grad)) <= 1e-7, name
 
 
+@pytest.mark.parametrize("tq,tk,dv", [(3, 6, 3), (6, 3, 2), (1, 4, 3), (5, 1, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_non_square_matches_central_finite_differences(tq, tk, dv, causal):
+    """Tq != Tk (upper-left causal mask) and dv != d, against finite
+    differences of the forward: pins the gradients of the general shapes
+    (keys past the last query row get zero gradients under the mask)."""
+    rng = np.random.default_rng(100 + 10 * tq + tk)
+    d = 3
+    q, k = rng.normal(size=(tq, d)), rng.normal(size=(tk, d))
+    v, do = rng.normal(size=(tk, dv)), rng.normal(size=(tq, dv))
+    scale, h = 0.7, 1e-6
+    dq, dk, dv_, _ = oracle.attention_backward(q, k, v, do, scale, causal)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv_.shape == v.shape
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv_)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            fp = _objective(**{**args, name: xp}, do=do, scale=scale, causal=causal)
+            fm = _objective(**{**args, name: xm}, do=do, scale=scale, causal=causal)
+            fd[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(fd - grad)) <= 1e-7, name
+    if causal and tk > tq:
+        assert np.all(dk[tq:] == 0) and np.all(dv_[tq:] == 0)
+
+
 def test_backward_matches_torch_float64_autograd():
     rng = np.random.default_rng(19)
     for causal in (False, True):
