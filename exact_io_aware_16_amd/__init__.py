@@ -77,6 +77,9 @@ def library():
         lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, f, i, vp]
         lib.fa_fwd_strided.restype = i
         lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        lib.fa_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i64p, i64p, i64p, f, i,
+                                       vp]
+        lib.fa_bwd_strided.restype = i
         lib.fa_bwd_ex.restype = i
         lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd_noalloc.restype = i
@@ -213,8 +216,8 @@ def forward_splitkv(q, k, v, causal=False, scale=None, n_splits=0, workspace=Non
     return o, l
 
 
-def _check_bwd(q, k, v, o, lse, do, square=True):
-    _check(q, k, v, square=square)
+def _check_bwd(q, k, v, o, lse, do, square=True, strided=False):
+    _check(q, k, v, square=square, strided=strided)
     if v.shape[3] != q.shape[3]:
         raise ValueError(f"backward: v needs the width of q and k (dv = d), got {tuple(v.shape)} for d = {q.shape[3]}")
     if q.dtype != torch.bfloat16 or do.dtype != torch.bfloat16:
@@ -257,18 +260,26 @@ def backward(q, k, v, o, lse, do, causal=False, scale=None, workspace=None):
     ``o`` and ``lse`` must be the forward's outputs for the same inputs; the
     probability tiles are recomputed from them.  bf16 inputs only.  Q may
     have a different number of rows than K and V (fa_bwd_ex, upper-left
-    causal mask), V the width of Q and K.
+    causal mask), V the width of Q and K.  With one row count, Q, K and V
+    may be views with a unit head-dim stride, such as slices of a packed QKV
+    tensor (fa_bwd_strided; K and V sharing a row stride).
     """
-    _check_bwd(q, k, v, o, lse, do, square=False)
+    strided = not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous())
+    _check_bwd(q, k, v, o, lse, do, square=False, strided=strided)
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
+    if strided and Nq != Nk:
+        raise ValueError("strided views take one row count for Q, K and V")
     workspace = workspace_for(q, workspace)
     dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
     dk = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
     dv = torch.empty_like(dk)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace))
     tail = (_scale(scale, d), int(bool(causal)), _stream(q.device))
-    if Nq == Nk:
+    if strided:
+        arr = lambda t: (ctypes.c_int64 * 3)(*t.stride()[:3])
+        name, st = "fa_bwd_strided", library().fa_bwd_strided(*args, B, H, Nq, d, arr(q), arr(k), arr(v), *tail)
+    elif Nq == Nk:
         name, st = "fa_bwd", library().fa_bwd(*args, B, H, Nq, d, *tail)
     else:
         name, st = "fa_bwd_ex", library().fa_bwd_ex(*args, B, H, Nq, Nk, d, *tail)

@@ -247,6 +247,27 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const float* o, const
                                         Nq, Nk, d, scale, causal, nullptr, nullptr, stream));
 }
 
+int fa_bwd_strided(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                   float* dq, float* dk, float* dv, void* workspace, int B, int H, int N, int d,
+                   const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides, float scale,
+                   int causal, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, H, N, d, causal, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if ((st = check_strides(q, q_strides, N, d)) != FA_OK) return st;
+  if ((st = check_strides(k, k_strides, N, d)) != FA_OK) return st;
+  if ((st = check_strides(v, v_strides, N, d)) != FA_OK) return st;
+  if (k_strides[2] != v_strides[2]) return FA_ERR_SHAPE;  // K and V rows share one stride
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!workspace) return FA_ERR_WORKSPACE;
+  const fa::Strides lay{q_strides[0], q_strides[1], k_strides[0], k_strides[1], v_strides[0], v_strides[1],
+                        (int)q_strides[2],  (int)k_strides[2],  (int)v_strides[2],  H};
+  return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B * H,
+                                        N, N, d, scale, causal, nullptr, nullptr, stream, &lay));
+}
+
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
                    float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
                    hipStream_t stream) {

@@ -105,29 +105,31 @@ struct DkdvSmem {
 
 // 16-byte chunks a thread copies for one BQ x D query tile: LDS block
 // (i*4 + wave) of 1 KiB, lane l -> row r, slot s; the source is row
-// perm32(r) (within 32) and chunk s ^ swz(r).
+// perm32(r) (within 32) and chunk s ^ swz(r), rows row_bytes apart in memory.
 template <int D>
 struct QCopy {
   static constexpr int SLOTS = D / 8;
   static constexpr int ROWS_PER_INSTR = 64 / SLOTS;
   static constexpr int INSTR = kBQ * SLOTS / kThreads;
   uint32_t off[INSTR];
-  __device__ __forceinline__ void init(int wave, int lane) {
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes) {
 #pragma unroll
     for (int i = 0; i < INSTR; ++i) {
       const int r = (i * kWaves + wave) * ROWS_PER_INSTR + lane / SLOTS;
       const int slot = lane % SLOTS;
-      off[i] = (uint32_t)(((r & ~31) + perm32(r & 31)) * D * 2 + 16 * (slot ^ swz<D * 2>(r)));
+      off[i] = (uint32_t)((r & ~31) + perm32(r & 31)) * row_bytes + (uint32_t)(16 * (slot ^ swz<D * 2>(r)));
     }
   }
 };
 
-template <int D, bool CAUSAL, bool DROP>
+// STRIDED: Q, K, V are views (lay: element strides of batch, head and row);
+// otherwise dense, with the layout compiled in.
+template <int D, bool CAUSAL, bool DROP, bool STRIDED>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     const bf16_raw* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dsc,
     float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, int n_kvblk, int total, float scale, float c,
-    Dropout drop, Seqs seqs) {
+    Dropout drop, Seqs seqs, Strides lay) {
   constexpr int NKK = D / 16;  // 16-wide head-dim slices (contraction of S and dP)
   constexpr int NDB = D / 32;  // 32-row blocks of dK^T / dV^T
   constexpr int RB = D * 2;    // bytes per Q / dO / K row
@@ -163,6 +165,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     if (kvb * kBKV >= Nk) return;  // past the end of a shorter sequence
   }
   const size_t head = row0 * D, khead = krow0 * D;
+  // Q, K, V bases and row strides (elements); dO, the statistics and the
+  // gradients are always dense
+  const bf16_raw *Qh = Q + head, *Kh = K + khead, *Vh = V + khead;
+  int q_stride = D, k_stride = D, v_stride = D;
+  if constexpr (STRIDED) {
+    const int b = bh / lay.H, hh = bh - b * lay.H;
+    Qh = Q + (size_t)(b * lay.qb + hh * lay.qh);
+    Kh = K + (size_t)(b * lay.kb + hh * lay.kh);
+    Vh = V + (size_t)(b * lay.vb + hh * lay.vh);
+    q_stride = lay.qr;
+    k_stride = lay.kr;
+    v_stride = lay.vr;
+  }
 
   const int k0 = kvb * kBKV;
   const int my_key = k0 + 32 * wave + col;
@@ -183,14 +198,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     return;  // workgroup-uniform: every wave leaves before any barrier
   }
 
-  const int head_bytes = Nq * D * 2, khead_bytes = Nk * D * 2;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + khead), (short)0, khead_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + khead), (short)0, khead_bytes, 0x00020000);
+  // byte spans of a head's rows: up to the end of the last row, D elements
+  const uint32_t q_row = (uint32_t)q_stride * 2u, k_row = (uint32_t)k_stride * 2u, v_row = (uint32_t)v_stride * 2u;
+  const int head_bytes = Nq * D * 2;
+  const int k_bytes = (int)((uint32_t)(Nk - 1) * k_row + (uint32_t)(D * 2));
+  const int v_bytes = (int)((uint32_t)(Nk - 1) * v_row + (uint32_t)(D * 2));
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, k_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, v_bytes, 0x00020000);
 
-  QCopy<D> qc;
-  qc.init(wave, lane);
+  // copy offsets: Q rows q_row apart; dO rows dense (a set of their own only
+  // when Q is strided)
+  QCopy<D> qc, gc;
+  qc.init(wave, lane, q_row);
+  if constexpr (STRIDED) gc.init(wave, lane, (uint32_t)(D * 2));
+  const QCopy<D>& gq = STRIDED ? gc : qc;
   // the wave index in a scalar register: the copies' LDS addresses (M0) are
   // scalar arithmetic
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -201,15 +222,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   auto issue_qtile = [&](uint32_t b, int q0) {
     q0 = __builtin_amdgcn_readfirstlane(q0);
     const uint32_t toff = (uint32_t)q0 * D * 2, rest = (uint32_t)head_bytes - toff;
-    const __amdgpu_buffer_rsrc_t qt =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Q + head + (size_t)q0 * D), (short)0, (int)rest, 0x00020000);
+    const uint32_t qrest = STRIDED ? (uint32_t)(Nq - 1 - q0) * q_row + (uint32_t)(D * 2) : rest;
+    const __amdgpu_buffer_rsrc_t qt = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Qh + (size_t)q0 * q_stride), (short)0, (int)qrest, 0x00020000);
     const __amdgpu_buffer_rsrc_t gt =
         __builtin_amdgcn_make_buffer_rsrc((void*)(dO + head + (size_t)q0 * D), (short)0, (int)rest, 0x00020000);
     const uint32_t qb = lds_addr_of(sm.q[b]), gb = lds_addr_of(sm.dout[b]);
 #pragma unroll
     for (int i = 0; i < QCopy<D>::INSTR; ++i) {
       lds_copy(qt, qc.off[i], 0u, qb + (uint32_t)(i * kWaves + wave_s) * 1024u);
-      lds_copy(gt, qc.off[i], 0u, gb + (uint32_t)(i * kWaves + wave_s) * 1024u);
+      lds_copy(gt, gq.off[i], 0u, gb + (uint32_t)(i * kWaves + wave_s) * 1024u);
     }
     if (wave_s < 2) {
       const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
@@ -226,9 +248,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   bf16x8 kres[NKK], vres[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    const uint32_t off = (uint32_t)(my_key * D + 16 * kk + 8 * g) * 2u;
-    kres[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
-    vres[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+    const uint32_t col_b = (uint32_t)(16 * kk + 8 * g) * 2u;
+    kres[kk] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (uint32_t)my_key * k_row + col_b, 0, 0));
+    vres[kk] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, (uint32_t)my_key * v_row + col_b, 0, 0));
   }
   // kept in AGPRs, which the matrix cores read directly.  The pins follow
   // all of the loads: a pin reads its register, so a pin right behind its
@@ -628,20 +652,20 @@ long long workspace_rows(int BH, int Nq, const Seqs& sq) {
   return sq.cu ? (long long)sq.H * sq.total : (long long)BH * Nq;
 }
 
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, bool STRIDED = false>
 hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws, float* dk,
                        float* dv, int BH, int Nq, int Nk, float scale, const Dropout& drop, const Seqs& sq,
-                       hipStream_t stream) {
+                       const Strides& lay, hipStream_t stream) {
   const long long rows = workspace_rows(BH, Nq, sq);
   const int n_kvblk = (Nk + kBKV - 1) / kBKV;
   const long long total = (long long)BH * n_kvblk;
   if (total == 0) return hipSuccess;  // no keys: no dK, dV
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROP>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DROP, STRIDED>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k), static_cast<const bf16_raw*>(v),
                      static_cast<const bf16_raw*>(dout), ws + rows, ws, dk, dv, Nq, Nk, n_kvblk, (int)total, scale,
-                     scale * kLog2e, drop, sq);
+                     scale * kLog2e, drop, sq, lay);
   return hipGetLastError();
 }
 
@@ -656,38 +680,45 @@ hipError_t launch_bwd_prep(const void* dout, const float* o, const float* lse, f
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_drop(const void* q, const void* k, const void* v, const void* dout, const float* ws,
                             float* dk, float* dv, int BH, int Nq, int Nk, float scale, const Dropout* drop,
-                            const Seqs& sq, hipStream_t stream) {
+                            const Seqs& sq, const Strides* lay, hipStream_t stream) {
+  if (lay) {
+    // strided views: dense packing of sequences and dropout are not offered
+    if (drop || sq.cu) return hipErrorInvalidValue;
+    return launch_dkdv<D, CAUSAL, false, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, Dropout{}, sq, *lay,
+                                               stream);
+  }
+  const Strides dense = dense_strides(Nq, Nk, D);
   if (drop) {
     if (sq.cu) return hipErrorInvalidValue;  // dropout is offered for the dense layout only
-    return launch_dkdv<D, CAUSAL, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, *drop, sq, stream);
+    return launch_dkdv<D, CAUSAL, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, *drop, sq, dense, stream);
   }
-  return launch_dkdv<D, CAUSAL, false>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, Dropout{}, sq, stream);
+  return launch_dkdv<D, CAUSAL, false>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, Dropout{}, sq, dense, stream);
 }
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws,
                            float* dk, float* dv, int BH, int Nq, int Nk, int d, float scale, int causal,
-                           const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+                           const Dropout* drop, const Seqs* seqs, hipStream_t stream, const Strides* lay) {
   const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
   if (d == 128)
-    return causal ? launch_dkdv_drop<128, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, stream)
-                  : launch_dkdv_drop<128, false>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, stream);
-  return causal ? launch_dkdv_drop<64, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, stream)
-                : launch_dkdv_drop<64, false>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, stream);
+    return causal ? launch_dkdv_drop<128, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, lay, stream)
+                  : launch_dkdv_drop<128, false>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, lay, stream);
+  return causal ? launch_dkdv_drop<64, true>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, lay, stream)
+                : launch_dkdv_drop<64, false>(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, scale, drop, sq, lay, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* ws, int BH, int Nq, int Nk,
                            int d, float scale, int causal, const Dropout* drop, const Seqs* seqs,
-                           hipStream_t stream) {
+                           hipStream_t stream, const Strides* lay) {
   const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
   const long long rows = workspace_rows(BH, Nq, sq);
   // The dQ pass computes the row statistics of its own rows (the
   // preprocess, fused: every row belongs to exactly one of its workgroups)
   // and stores them for the dK/dV pass, which runs after it on the stream.
   hipError_t e = launch_bwd_dq_fused(q, k, v, dout, o, lse, ws + rows, ws, dq, BH, Nq, Nk, d, scale, causal, drop,
-                                     seqs, stream);
+                                     seqs, stream, lay);
   if (e != hipSuccess) return e;
-  return launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, d, scale, causal, drop, seqs, stream);
+  return launch_bwd_dkdv(q, k, v, dout, ws, dk, dv, BH, Nq, Nk, d, scale, causal, drop, seqs, stream, lay);
 }
 
 }  // namespace fa

@@ -66,12 +66,13 @@ struct KvCopy {
   static constexpr int ROWS_PER_INSTR = 64 / SLOTS;
   static constexpr int INSTR = BC * SLOTS / kThreads;
   uint32_t off[INSTR];
-  __device__ __forceinline__ void init(int wave, int lane) {
+  // row_bytes: distance of consecutive K (and V) rows in memory
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes) {
 #pragma unroll
     for (int i = 0; i < INSTR; ++i) {
       const int r = (i * kWaves + wave) * ROWS_PER_INSTR + lane / SLOTS;
       const int slot = lane % SLOTS;
-      off[i] = (uint32_t)(((r & ~31) + perm32(r & 31)) * D * 2 + 16 * (slot ^ swz<D * 2>(r)));
+      off[i] = (uint32_t)((r & ~31) + perm32(r & 31)) * row_bytes + (uint32_t)(16 * (slot ^ swz<D * 2>(r)));
     }
   }
 };
@@ -80,12 +81,14 @@ struct KvCopy {
 // L log2(e)) are computed here from O and L for this workgroup's rows and
 // stored to L2 / Dsc for the dK/dV pass, which then runs after this one;
 // otherwise they are read from L2 / Dsc (written by bwd_pre_kernel).
-template <int D, bool CAUSAL, bool DROP, bool FUSED>
+// STRIDED: Q, K, V are views (lay: element strides of batch, head and row;
+// K and V share the row stride); otherwise dense, with the layout compiled in.
+template <int D, bool CAUSAL, bool DROP, bool FUSED, bool STRIDED>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const bf16_raw* __restrict__ Q, const bf16_raw* __restrict__ K, const bf16_raw* __restrict__ V,
     const bf16_raw* __restrict__ dO, float* __restrict__ L2, float* __restrict__ Dsc, const float* __restrict__ O,
     const float* __restrict__ LSE, float* __restrict__ dQ, int Nq, int Nk, int n_qblk, int total, float scale,
-    float c, Dropout drop, Seqs seqs) {
+    float c, Dropout drop, Seqs seqs, Strides lay) {
   constexpr int BC = DqTile<D>::BC;
   constexpr int NKB = BC / 32;  // 32-key blocks per tile
   constexpr int NKK = D / 16;   // 16-wide head-dim slices (contraction of S and dP)
@@ -123,7 +126,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     row0 = krow0 = (size_t)hh * seqs.total + s0;
     if (qblk * kBR >= Nq) return;  // past the end of a shorter sequence
   }
-  const size_t head = row0 * D, khead = krow0 * D;
+  const size_t head = row0 * D;
+  // Q, K, V bases and row strides (elements); dO, O, the statistics and dQ
+  // are always dense
+  const bf16_raw *Qh = Q + head, *Kh = K + krow0 * D, *Vh = V + krow0 * D;
+  int q_stride = D, kv_stride = D;
+  if constexpr (STRIDED) {
+    const int b = bh / lay.H, hh = bh - b * lay.H;
+    Qh = Q + (size_t)(b * lay.qb + hh * lay.qh);
+    Kh = K + (size_t)(b * lay.kb + hh * lay.kh);
+    Vh = V + (size_t)(b * lay.vb + hh * lay.vh);
+    q_stride = lay.qr;
+    kv_stride = lay.kr;
+  }
 
   const int q_start = qblk * kBR;
   const int q0w = q_start + 32 * wave;
@@ -144,9 +159,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     return;
   }
 
-  const int head_bytes = Nk * D * 2;
+  const uint32_t kv_row = (uint32_t)kv_stride * 2u;
   KvCopy<D> kc;
-  kc.init(wave, lane);
+  kc.init(wave, lane, kv_row);
   // the wave index in a scalar register: the copies' LDS addresses (M0) are
   // scalar arithmetic
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -155,11 +170,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   // loop invariant and rows past the end of the head read as zeros.
   auto issue_tile = [&](uint32_t b, int key0) {
     key0 = __builtin_amdgcn_readfirstlane(key0);
-    const uint32_t rest = (uint32_t)head_bytes - (uint32_t)key0 * D * 2;
-    const __amdgpu_buffer_rsrc_t kt =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(K + khead + (size_t)key0 * D), (short)0, (int)rest, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vt =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(V + khead + (size_t)key0 * D), (short)0, (int)rest, 0x00020000);
+    // the head's key rows from key0 on, up to the end of the last one
+    const uint32_t rest = STRIDED ? (uint32_t)(Nk - 1 - key0) * kv_row + (uint32_t)(D * 2)
+                                  : (uint32_t)(Nk * D * 2) - (uint32_t)key0 * D * 2;
+    const __amdgpu_buffer_rsrc_t kt = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Kh + (size_t)key0 * kv_stride), (short)0, (int)rest, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vt = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Vh + (size_t)key0 * kv_stride), (short)0, (int)rest, 0x00020000);
     const uint32_t kb = lds_addr_of(sm.k[b]), vb = lds_addr_of(sm.v[b]);
 #pragma unroll
     for (int i = 0; i < KvCopy<D>::INSTR; ++i) {
@@ -174,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   float l2q, dq_sc;
   {
     const int qr = min(my_q, Nq - 1);
-    const bf16_raw* Qrow = Q + head + (size_t)qr * D;
+    const bf16_raw* Qrow = Qh + (size_t)qr * q_stride;
     const bf16_raw* Grow = dO + head + (size_t)qr * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -551,64 +568,74 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 
 // o, lse non-null: the fused launch (statistics computed here and stored to
 // l2 / dsc); else l2 / dsc hold them already
-template <int D, bool CAUSAL, bool DROP>
+template <int D, bool CAUSAL, bool DROP, bool STRIDED = false>
 hipError_t launch(const void* q, const void* k, const void* v, const void* dout, float* l2, float* dsc,
                   const float* o, const float* lse, float* dq, int BH, int Nq, int Nk, float scale,
-                  const Dropout& drop, const Seqs& sq, hipStream_t stream) {
+                  const Dropout& drop, const Seqs& sq, const Strides& lay, hipStream_t stream) {
   const int n_qblk = (Nq + kBR - 1) / kBR;
   const long long total = (long long)BH * n_qblk;
   if (total == 0) return hipSuccess;  // no query rows: no dQ
   if (total > (1LL << 30)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 7) / 8 * 8);
   if (o)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP, true>), dim3(grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP, true, STRIDED>), dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
                        static_cast<const bf16_raw*>(v), static_cast<const bf16_raw*>(dout), l2, dsc, o, lse, dq, Nq,
-                       Nk, n_qblk, (int)total, scale, scale * kLog2e, drop, sq);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       Nk, n_qblk, (int)total, scale, scale * kLog2e, drop, sq, lay);
+  else if constexpr (!STRIDED)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, DROP, false, false>), dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const bf16_raw*>(q), static_cast<const bf16_raw*>(k),
                        static_cast<const bf16_raw*>(v), static_cast<const bf16_raw*>(dout), l2, dsc, o, lse, dq, Nq,
-                       Nk, n_qblk, (int)total, scale, scale * kLog2e, drop, sq);
+                       Nk, n_qblk, (int)total, scale, scale * kLog2e, drop, sq, lay);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_drop(const void* q, const void* k, const void* v, const void* dout, float* l2, float* dsc,
                        const float* o, const float* lse, float* dq, int BH, int Nq, int Nk, float scale,
-                       const Dropout* drop, const Seqs& sq, hipStream_t stream) {
+                       const Dropout* drop, const Seqs& sq, const Strides* lay, hipStream_t stream) {
+  if (lay) {
+    // strided views: the fused launch only, without packing or dropout
+    if (drop || sq.cu || !o) return hipErrorInvalidValue;
+    return launch<D, CAUSAL, false, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, Dropout{}, sq, *lay,
+                                          stream);
+  }
+  const Strides dense = dense_strides(Nq, Nk, D);
   if (drop) {
     if (sq.cu) return hipErrorInvalidValue;  // dropout is offered for the dense layout only
-    return launch<D, CAUSAL, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, *drop, sq, stream);
+    return launch<D, CAUSAL, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, *drop, sq, dense, stream);
   }
-  return launch<D, CAUSAL, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, Dropout{}, sq, stream);
+  return launch<D, CAUSAL, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, Dropout{}, sq, dense,
+                                  stream);
 }
 
 hipError_t launch_any(const void* q, const void* k, const void* v, const void* dout, float* l2, float* dsc,
                       const float* o, const float* lse, float* dq, int BH, int Nq, int Nk, int d, float scale,
-                      int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+                      int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream, const Strides* lay) {
   const Seqs sq = seqs ? *seqs : Seqs{nullptr, 0, 0};
   if (d == 128)
-    return causal ? launch_drop<128, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, stream)
-                  : launch_drop<128, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, stream);
-  return causal ? launch_drop<64, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, stream)
-                : launch_drop<64, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, stream);
+    return causal
+               ? launch_drop<128, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, lay, stream)
+               : launch_drop<128, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, lay, stream);
+  return causal ? launch_drop<64, true>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, lay, stream)
+                : launch_drop<64, false>(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, scale, drop, sq, lay, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
                               const float* dsc, float* dq, int BH, int Nq, int Nk, int d, float scale, int causal,
-                              const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
+                              const Dropout* drop, const Seqs* seqs, hipStream_t stream, const Strides* lay) {
   // statistics only read on this launch
   return launch_any(q, k, v, dout, const_cast<float*>(l2), const_cast<float*>(dsc), nullptr, nullptr, dq, BH, Nq,
-                    Nk, d, scale, causal, drop, seqs, stream);
+                    Nk, d, scale, causal, drop, seqs, stream, lay);
 }
 
 hipError_t launch_bwd_dq_fused(const void* q, const void* k, const void* v, const void* dout, const float* o,
                                const float* lse, float* l2, float* dsc, float* dq, int BH, int Nq, int Nk, int d,
-                               float scale, int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream) {
-  return launch_any(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, d, scale, causal, drop, seqs, stream);
+                               float scale, int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream,
+                               const Strides* lay) {
+  return launch_any(q, k, v, dout, l2, dsc, o, lse, dq, BH, Nq, Nk, d, scale, causal, drop, seqs, stream, lay);
 }
 
 }  // namespace fa

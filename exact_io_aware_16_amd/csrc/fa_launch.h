@@ -24,6 +24,12 @@ struct Strides {
   int H;
 };
 
+// The strides of dense [BH, Nq, d] / [BH, Nk, d] inputs in this layout (one
+// head per batch entry).
+inline Strides dense_strides(int Nq, int Nk, int d) {
+  return Strides{(long long)Nq * d, 0, (long long)Nk * d, 0, (long long)Nk * d, 0, d, d, d, 1};
+}
+
 // Forward, bf16 inputs: Q [BH, Nq, d], K [BH, Nk, d], V [BH, Nk, dv].
 // n_ksplit > 1 cuts the key tiles into that many ranges processed by separate
 // workgroups; ws then holds n_ksplit * BH * Nq * (dv + 1) floats of partial
@@ -61,13 +67,15 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 // and Nk keys per head (upper-left causal mask when they differ).
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* l2,
                               const float* dsc, float* dq, int BH, int Nq, int Nk, int d, float scale, int causal,
-                              const Dropout* drop, const Seqs* seqs, hipStream_t stream);
+                              const Dropout* drop, const Seqs* seqs, hipStream_t stream,
+                              const Strides* lay = nullptr);
 // The dQ pass with the preprocess fused in: computes scale D = scale dO . O and
 // L log2(e) of its rows from o and lse (bitwise as launch_bwd_prep does),
 // stores them to l2 / dsc for a dK/dV launch that follows, and writes dq.
 hipError_t launch_bwd_dq_fused(const void* q, const void* k, const void* v, const void* dout, const float* o,
                                const float* lse, float* l2, float* dsc, float* dq, int BH, int Nq, int Nk, int d,
-                               float scale, int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream);
+                               float scale, int causal, const Dropout* drop, const Seqs* seqs, hipStream_t stream,
+                               const Strides* lay = nullptr);
 
 // Backward phases (fa_bwd.hip); ws holds [scale * D | L log2(e)], one float
 // each per query row (BH * Nq).  The preprocess works on query rows only.
@@ -75,7 +83,8 @@ hipError_t launch_bwd_prep(const void* dout, const float* o, const float* lse, f
                            float scale, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* ws,
                            float* dk, float* dv, int BH, int Nq, int Nk, int d, float scale, int causal,
-                           const Dropout* drop, const Seqs* seqs, hipStream_t stream);
+                           const Dropout* drop, const Seqs* seqs, hipStream_t stream,
+                           const Strides* lay = nullptr);
 
 // The allocation-free backward's scratch (fa_scratch.hip): its capacity in
 // floats, and its device address on the current device (looked up once per
@@ -83,9 +92,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 size_t scratch_floats();
 hipError_t scratch_on_current_device(float** out);
 
+// lay: element strides of strided Q, K, V (batch, head, row; K and V share
+// the row stride), null for dense inputs; dO, O, L and the gradients are
+// always dense.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* dvec, int BH, int Nq, int Nk,
                            int d, float scale, int causal, const Dropout* drop, const Seqs* seqs,
-                           hipStream_t stream);
+                           hipStream_t stream, const Strides* lay = nullptr);
 
 }  // namespace fa

@@ -194,6 +194,24 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const float* o, const
               int B, int H, int Nq, int Nk, int d, float scale, int causal, hipStream_t stream);
 
 /*
+ * fa_bwd on strided Q, K, V: the backward of fa_fwd_strided with Nq = Nk = N
+ * and dv = d (for example Q, K, V as slices of one packed QKV projection;
+ * "Build it" takes any tensor).  Same arguments, results, stream behaviour
+ * and errors as fa_bwd, plus
+ *   q_strides, k_strides, v_strides : host arrays of 3 element strides
+ *     (batch, head, row) of Q, K, V; the head-dim stride is 1.
+ * Each stride must be >= 0 and a multiple of 8, a row stride at least d and
+ * below 2^31, one head's rows byte-addressable in 31 bits, q, k, v 16-byte
+ * aligned, and K and V must share their row stride; otherwise FA_ERR_SHAPE
+ * (NULL stride arrays: FA_ERR_NULL).  dout, o, lse and dq, dk, dv are dense
+ * [B,H,N,d] (lse [B,H,N]); the gradients are those of the viewed tensors.
+ */
+int fa_bwd_strided(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                   const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                   int B, int H, int N, int d, const int64_t* q_strides, const int64_t* k_strides,
+                   const int64_t* v_strides, float scale, int causal, hipStream_t stream);
+
+/*
  * fa_bwd without a workspace argument, for callers that cannot allocate
  * device memory (code being captured into a HIP graph, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, layouts, results and

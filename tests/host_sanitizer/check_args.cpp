@@ -191,6 +191,24 @@ int main() {
   EXPECT(bwd_ex(INT_MAX, INT_MAX, 8, 5, 128, 0.125f, 1), FA_ERR_SHAPE);
   EXPECT(bwd_ex(2, 16, 4096, 1000, 128, 0.125f, 1), FA_ERR_HIP);
 
+  // ---- backward on strided inputs
+  {
+    const int64_t dense[3] = {2 * 8 * 64, 8 * 64, 64}, packed[3] = {8 * 3 * 2 * 64, 64, 3 * 2 * 64};
+    const int64_t narrow[3] = {0, 0, 56}, odd[3] = {0, 0, 68}, wide[3] = {0, 0, 1 << 30};
+    auto sb = [&](const int64_t* qs, const int64_t* ks, const int64_t* vs, int N = 8, void* ws = P) {
+      return fa_bwd_strided(P, P, P, F, F, P, F, F, F, ws, 1, 2, N, 64, qs, ks, vs, 0.125f, 1, nullptr);
+    };
+    EXPECT(sb(packed, packed, packed), FA_ERR_HIP);
+    EXPECT(sb(dense, packed, packed), FA_ERR_HIP);
+    EXPECT(sb(packed, dense, packed), FA_ERR_SHAPE);  // K and V row strides differ
+    EXPECT(sb(narrow, packed, packed), FA_ERR_SHAPE);
+    EXPECT(sb(packed, odd, odd), FA_ERR_SHAPE);
+    EXPECT(sb(packed, wide, wide), FA_ERR_SHAPE);     // one head past 2^31 bytes
+    EXPECT(sb(nullptr, packed, packed), FA_ERR_NULL);
+    EXPECT(sb(packed, packed, packed, 8, nullptr), FA_ERR_WORKSPACE);
+    EXPECT(sb(packed, packed, packed, 0, nullptr), FA_OK);
+  }
+
   // ---- the backward phases
   EXPECT(fa_bwd_prep(P, F, F, P, 1, 2, 8, 96, 0.1f, nullptr), FA_ERR_HEADDIM);
   EXPECT(fa_bwd_prep(P, F, F, nullptr, 1, 2, 8, 64, 0.1f, nullptr), FA_ERR_WORKSPACE);

@@ -22,7 +22,8 @@ hipError_t launch_fwd_f32(const float*, const float*, const float*, float*, floa
 }
 
 hipError_t launch_bwd_dq_bf16(const void*, const void*, const void*, const void*, const float*, const float*, float*,
-                              int, int, int, int, float, int, const Dropout*, const Seqs*, hipStream_t) {
+                              int, int, int, int, float, int, const Dropout*, const Seqs*, hipStream_t,
+                              const Strides*) {
   ++g_launches;
   return hipErrorNotSupported;
 }
@@ -33,14 +34,14 @@ hipError_t launch_bwd_prep(const void*, const float*, const float*, float*, int,
 }
 
 hipError_t launch_bwd_dkdv(const void*, const void*, const void*, const void*, const float*, float*, float*, int, int,
-                           int, int, float, int, const Dropout*, const Seqs*, hipStream_t) {
+                           int, int, float, int, const Dropout*, const Seqs*, hipStream_t, const Strides*) {
   ++g_launches;
   return hipErrorNotSupported;
 }
 
 hipError_t launch_bwd_bf16(const void*, const void*, const void*, const float*, const float*, const void*, float*,
                            float*, float*, float*, int, int, int, int, float, int, const Dropout*, const Seqs*,
-                           hipStream_t) {
+                           hipStream_t, const Strides*) {
   ++g_launches;
   return hipErrorNotSupported;
 }

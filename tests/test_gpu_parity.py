@@ -821,6 +821,52 @@ def test_fwd_strided_views_of_packed_qkv(d, causal):
     check_fwd(o_s.cpu().numpy(), l_s.cpu().numpy(), oref, lref, f"strided d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [300, 1000])
+def test_bwd_strided_views_of_packed_qkv(N, d, causal):
+    """The backward on Q, K, V as views of one packed [B, N, 3, H, d]
+    projection (fa_bwd_strided): bitwise the gradients of the contiguous
+    copies, and the oracle's."""
+    B, H = 2, 3
+    g = torch.Generator("cpu").manual_seed(850 + d + N)
+    qkv = torch.randn((B, N, 3, H, d), generator=g).to(torch.bfloat16)
+    do = I.draw((B, H, N, d), 860 + d + N)
+    views = [qkv[:, :, j].permute(0, 2, 1, 3) for j in range(3)]
+    say(f"strided backward N={N} d={d} causal={causal}")
+    gqkv, gdo = qkv.cuda(), do.cuda()
+    gviews = [gqkv[:, :, j].permute(0, 2, 1, 3) for j in range(3)]
+    assert not gviews[0].is_contiguous()
+    o, l = fa.forward(*gviews, causal=causal)
+    got = fa.backward(*gviews, o, l, gdo, causal=causal)
+    ref_c = fa.backward(*[x.contiguous() for x in gviews], o, l, gdo, causal=causal)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(got, ref_c):
+        assert torch.equal(a_, b_)
+    t = {"q": views[0].contiguous(), "k": views[1].contiguous(), "v": views[2].contiguous(), "do": do}
+    check_bwd([x.cpu().numpy() for x in got], oracle_bwd(t, causal, 1 / math.sqrt(d)),
+              f"strided bwd N={N} d={d} causal={causal}")
+
+
+def test_bwd_strided_padded_heads():
+    """Head strides larger than the rows (Q, K, V carved out of wider padded
+    buffers, K and V sharing a row stride): the contiguous copies' gradients."""
+    B, H, N, d = 2, 2, 257, 128
+    gq = I.draw((B, H, N + 3, d + 64), 870).cuda()
+    gkv = I.draw((B, N, 2, H, d + 16), 871).cuda()
+    q = gq[:, :, 2:N + 2, 32:32 + d]
+    k = gkv[:, :, 0, :, 8:8 + d].permute(0, 2, 1, 3)
+    v = gkv[:, :, 1, :, 0:d].permute(0, 2, 1, 3)
+    do = I.draw((B, H, N, d), 872).cuda()
+    say("strided backward, padded heads")
+    o, l = fa.forward(q, k, v, causal=True)
+    got = fa.backward(q, k, v, o, l, do, causal=True)
+    ref_c = fa.backward(q.contiguous(), k.contiguous(), v.contiguous(), o, l, do, causal=True)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(got, ref_c):
+        assert torch.equal(a_, b_)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_strided_general_shapes(causal):
     """Tq != Tk and dv != d with K, V sliced from wider buffers and Q taken
